@@ -1,0 +1,416 @@
+/*
+ * dit_oracle.c -- plain, slow CPU oracle for the BF16 DiT row epilogues.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file defines the expected result of every
+ * epilogue so the GPU kernels can be checked against it.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it;
+ * the product path never calls it and shares no code with it.
+ *
+ * Arithmetic model (the rounding contract):
+ *   - every floating-point step is one IEEE-754 binary32 operation with
+ *     round-to-nearest-even: add, sub, mul, div, sqrt.  No fused multiply-add
+ *     (built with -ffp-contract=off), no flush of subnormals.
+ *   - bf(v): binary32 -> bfloat16, round-to-nearest-even, written here with
+ *     integer operations on the bit pattern.  A bf16 value read back is its
+ *     exact binary32 value (the 16 bits moved to the top half).
+ *   - row sums follow one declared order, R(D): a wave of 64 lanes, lane l
+ *     owning elements 512c + 8l + j (j = 0..7) of chunk c; each lane sums its
+ *     own elements from +0 in (c, j) order, then lanes combine pairwise with
+ *     partners l^1, l^2, l^4, l^8, l^16, l^32.  Head sums (Q/K norm) use the
+ *     same rule with Dh/8 lanes and a single chunk.
+ *
+ * Sources (pages on SGLang's diffusion kernels):
+ *   [P1] "基于Agent的SGLang扩散模型Kernel优化实践：Qwen-Image、FLUX.2和视频模型"
+ *        (tahou.com), sections "数学等价不代表结果完全一致" (AdaLN rounding
+ *        points), "合并QKV投影时的数值问题" (QKV epilogue steps),
+ *        "Wan视频模型的数据搬运优化" (per-token modulation rows).
+ *   [P3] "#34085 [diffusion] Clean up kernels and shared fast paths"
+ *        (prhub.com.cn), sections "实现拆解" and "关键源码片段" (the native
+ *        bf16 RMSNorm-scale chain and its guards).
+ *   [P4] "AI Agent 驱动的 SGLang Kernel 一等公民" (163.com), section 0x3, 3.2
+ *        (the DiT fusions table: rmsnorm+tanh(gate)*x+residual, QK-norm+RoPE,
+ *        residual+gate*update).
+ *
+ * Parity status: every function here is pinned by the CPU tests except the
+ * reduction order itself, which is a declaration (its effect is pinned by a
+ * hand-derived order-sensitive case).  See the tests for the pins.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "dit_oracle.h"
+
+/* ------------------------------------------------------------------------- */
+/* bfloat16 emulation                                                        */
+/* ------------------------------------------------------------------------- */
+
+static uint32_t f32_bits(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  return u;
+}
+
+static float bits_f32(uint32_t u) {
+  float v;
+  memcpy(&v, &u, 4);
+  return v;
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even.  NaN stays NaN (quiet
+ * bit set, sign kept); finite values that round past the largest bf16 become
+ * infinities; subnormals are kept. */
+uint16_t orc_bf16_round(float v) {
+  uint32_t u = f32_bits(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+float orc_bf16_value(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+/* Correctly rounded bfloat16 of a binary64 value (used only for tanh, whose
+ * exact value is approximated in double).  The value is scaled by a power of
+ * two so that one bf16 ulp becomes 1.0, rounded to an integer with the
+ * default ties-to-even mode, and scaled back; all scalings are exact. */
+uint16_t orc_bf16_round_f64(double v) {
+  if (isnan(v)) return 0x7FC0;
+  if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;
+  if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e);                 /* a = m * 2^e, 0.5 <= m < 1 */
+  int ulp_exp = e - 8;          /* 8 significant bits */
+  if (ulp_exp < -133) ulp_exp = -133; /* bf16 subnormal spacing */
+  double q = nearbyint(ldexp(a, -ulp_exp));
+  double r = ldexp(q, ulp_exp);
+  float rf = (float)r;          /* exact: r has at most 8 significant bits */
+  if (isinf(rf) || r > 3.3895313892515355e38) rf = INFINITY;
+  uint16_t h = (uint16_t)(f32_bits(rf) >> 16);
+  return signbit(v) ? (uint16_t)(h | 0x8000u) : h;
+}
+
+static float bfv(float v) { return orc_bf16_value(orc_bf16_round(v)); }
+
+/* ------------------------------------------------------------------------- */
+/* Declared reduction orders                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* R(D): 64 lanes, 8-element vectors, chunks of 512 elements. */
+float orc_sum_wave(const float *t, int64_t D) {
+  float p[64];
+  int64_t chunks = (D + 511) / 512;
+  for (int l = 0; l < 64; ++l) {
+    p[l] = 0.0f;
+    for (int64_t c = 0; c < chunks; ++c)
+      for (int j = 0; j < 8; ++j) {
+        int64_t e = 512 * c + 8 * l + j;
+        if (e < D) p[l] = p[l] + t[e];
+      }
+  }
+  for (int m = 1; m < 64; m <<= 1) {
+    float q[64];
+    for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ m];
+    memcpy(p, q, sizeof p);
+  }
+  return p[0];
+}
+
+/* Head sum: Dh/8 lanes (a power of two, at most 64), one chunk. */
+float orc_sum_head(const float *t, int64_t Dh) {
+  float p[64];
+  int lanes = (int)(Dh / 8);
+  for (int l = 0; l < lanes; ++l) {
+    p[l] = 0.0f;
+    for (int j = 0; j < 8; ++j) p[l] = p[l] + t[8 * l + j];
+  }
+  for (int m = 1; m < lanes; m <<= 1) {
+    float q[64];
+    for (int l = 0; l < lanes; ++l) q[l] = p[l] + p[l ^ m];
+    memcpy(p, q, sizeof p);
+  }
+  return p[0];
+}
+
+/* ------------------------------------------------------------------------- */
+/* Single-input bf16 steps                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* s1 = bf(1 + scale): the "(1 + scale)" tensor of AdaLN, rounded where the
+ * eager chain materialises it [P1 数学等价不代表结果完全一致]. */
+uint16_t orc_one_plus(uint16_t scale) {
+  return orc_bf16_round(1.0f + orc_bf16_value(scale));
+}
+
+/* T(g): correctly rounded bf16 of tanh(g) for a bf16 gate g.  tanh is
+ * evaluated in binary64 (error far below the bf16 rounding margin, which the
+ * tests check against long double over all 65536 inputs) and rounded once. */
+uint16_t orc_tanh(uint16_t g) {
+  float v = orc_bf16_value(g);
+  if (isnan(v)) return (uint16_t)(g | 0x0040u);
+  return orc_bf16_round_f64(tanh((double)v));
+}
+
+/* RMSNorm rstd from the bf16 value v = bf(ms + eps): bf(1 / sqrt(v)), with an
+ * IEEE square root and an IEEE division (the lossless reading of the rsqrt in
+ * the native bf16 RMSNorm chain [P3 关键源码片段]). */
+uint16_t orc_rms_rstd(uint16_t v) {
+  return orc_bf16_round(1.0f / sqrtf(orc_bf16_value(v)));
+}
+
+/* ------------------------------------------------------------------------- */
+/* LayerNorm + AdaLN modulate  [P1 数学等价不代表结果完全一致]                   */
+/* ------------------------------------------------------------------------- */
+
+/* Two-pass LayerNorm of one row (no affine), rounded once to bf16.
+ * stats (optional) receives mu, var, rho. */
+void orc_ln_row(const uint16_t *x, int64_t D, float eps, uint16_t *n, float *stats) {
+  float *t = (float *)calloc((size_t)D + 1, sizeof(float));
+  float *d = (float *)calloc((size_t)D + 1, sizeof(float));
+  for (int64_t i = 0; i < D; ++i) t[i] = orc_bf16_value(x[i]);
+  float mean = orc_sum_wave(t, D) / (float)D;
+  for (int64_t i = 0; i < D; ++i) {
+    d[i] = t[i] - mean;
+    t[i] = d[i] * d[i];
+  }
+  float var = orc_sum_wave(t, D) / (float)D;
+  float rho = 1.0f / sqrtf(var + eps);
+  for (int64_t i = 0; i < D; ++i) n[i] = orc_bf16_round(d[i] * rho);
+  if (stats) {
+    stats[0] = mean;
+    stats[1] = var;
+    stats[2] = rho;
+  }
+  free(t);
+  free(d);
+}
+
+/* out = bf( bf( n * bf(1 + scale) ) + shift ), n = LN(x) in bf16. */
+int orc_ln_modulate(uint16_t *out, int64_t out_rs, const uint16_t *x, int64_t x_rs,
+                    const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
+                    int64_t mod_rows, int64_t rows, int64_t dim, float eps) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  uint16_t *n = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)dim);
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t *sc = scale + (r / per_mod) * mod_rs;
+    const uint16_t *sh = shift + (r / per_mod) * mod_rs;
+    orc_ln_row(x + r * x_rs, dim, eps, n, NULL);
+    for (int64_t i = 0; i < dim; ++i) {
+      float s1 = orc_bf16_value(orc_one_plus(sc[i]));
+      float p = bfv(orc_bf16_value(n[i]) * s1);
+      out[r * out_rs + i] = orc_bf16_round(p + orc_bf16_value(sh[i]));
+    }
+  }
+  free(n);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Native-bf16 RMSNorm chain  [P3 关键源码片段, rmsnorm_scale kernel]            */
+/* ------------------------------------------------------------------------- */
+
+/* y2 = bf(bf(x * rstd) * w), with every intermediate of the chain rounded to
+ * bf16: squares, mean square, mean square + eps, rstd. */
+void orc_rms_row(const uint16_t *x, const uint16_t *w, int64_t D, float eps, uint16_t *y2,
+                 float *stats) {
+  float *t = (float *)calloc((size_t)D + 1, sizeof(float));
+  for (int64_t i = 0; i < D; ++i) {
+    float xv = orc_bf16_value(x[i]);
+    t[i] = bfv(xv * xv);
+  }
+  uint16_t ms = orc_bf16_round(orc_sum_wave(t, D) / (float)D);
+  uint16_t v = orc_bf16_round(orc_bf16_value(ms) + eps);
+  uint16_t rstd = orc_rms_rstd(v);
+  float rv = orc_bf16_value(rstd);
+  for (int64_t i = 0; i < D; ++i) {
+    float y1 = bfv(orc_bf16_value(x[i]) * rv);
+    y2[i] = orc_bf16_round(y1 * orc_bf16_value(w[i]));
+  }
+  if (stats) {
+    stats[0] = orc_bf16_value(ms);
+    stats[1] = orc_bf16_value(v);
+    stats[2] = rv;
+  }
+  free(t);
+}
+
+/* out = bf(y2 * scale[m]) */
+int orc_rmsnorm_scale(uint16_t *out, int64_t out_rs, const uint16_t *x, int64_t x_rs,
+                      const uint16_t *w, const uint16_t *scale, int64_t mod_rs, int64_t mod_rows,
+                      int64_t rows, int64_t dim, float eps) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  uint16_t *y2 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)dim);
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t *sc = scale + (r / per_mod) * mod_rs;
+    orc_rms_row(x + r * x_rs, w, dim, eps, y2, NULL);
+    for (int64_t i = 0; i < dim; ++i)
+      out[r * out_rs + i] = orc_bf16_round(orc_bf16_value(y2[i]) * orc_bf16_value(sc[i]));
+  }
+  free(y2);
+  return 0;
+}
+
+/* out = bf(residual + bf(T(gate[m]) * y2))   [P4 0x3 3.2: rmsnorm+tanh(gate)*x+residual;
+ * P3 实现拆解: rmsnorm_tanh_residual shares the native bf16 RMSNorm chain] */
+int orc_rmsnorm_tanh_residual(uint16_t *out, int64_t out_rs, const uint16_t *x, int64_t x_rs,
+                              const uint16_t *residual, int64_t res_rs, const uint16_t *w,
+                              const uint16_t *gate, int64_t mod_rs, int64_t mod_rows,
+                              int64_t rows, int64_t dim, float eps) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  uint16_t *y2 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)dim);
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t *g = gate + (r / per_mod) * mod_rs;
+    const uint16_t *res = residual + r * res_rs;
+    orc_rms_row(x + r * x_rs, w, dim, eps, y2, NULL);
+    for (int64_t i = 0; i < dim; ++i) {
+      float tau = orc_bf16_value(orc_tanh(g[i]));
+      float q = bfv(tau * orc_bf16_value(y2[i]));
+      out[r * out_rs + i] = orc_bf16_round(orc_bf16_value(res[i]) + q);
+    }
+  }
+  free(y2);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Residual gate-add  [P1 将FP8量化融合到前序算子: residual + gate*(...);        */
+/*                     P4 0x3 3.2: residual + gate*update]                    */
+/* ------------------------------------------------------------------------- */
+
+int orc_residual_gate_add(uint16_t *out, int64_t out_rs, const uint16_t *residual,
+                          int64_t res_rs, const uint16_t *y, int64_t y_rs, const uint16_t *gate,
+                          int64_t mod_rs, int64_t mod_rows, int64_t rows, int64_t dim) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t *g = gate + (r / per_mod) * mod_rs;
+    for (int64_t i = 0; i < dim; ++i) {
+      float gy = bfv(orc_bf16_value(g[i]) * orc_bf16_value(y[r * y_rs + i]));
+      out[r * out_rs + i] = orc_bf16_round(orc_bf16_value(residual[r * res_rs + i]) + gy);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Q/K RMSNorm + interleaved RoPE + joint QKV write                          */
+/* [P1 合并QKV投影时的数值问题: the four steps of the epilogue]                 */
+/* ------------------------------------------------------------------------- */
+
+/* One head: u = bf(bf(x * rho) * w), rho = 1 / sqrt(sum(x*x)/Dh + eps) in
+ * binary32, then each adjacent pair (a, b) is rotated by the angle whose
+ * cosine and sine are c[i], z[i]: (a*c - b*z, a*z + b*c), rounded once. */
+void orc_qk_head(const uint16_t *x, const uint16_t *w, const float *c, const float *z,
+                 int64_t Dh, float eps, uint16_t *o) {
+  float t[1024];
+  float u[1024];
+  for (int64_t i = 0; i < Dh; ++i) {
+    float xv = orc_bf16_value(x[i]);
+    t[i] = xv * xv;
+  }
+  float ms = orc_sum_head(t, Dh) / (float)Dh;
+  float rho = 1.0f / sqrtf(ms + eps);
+  for (int64_t i = 0; i < Dh; ++i) {
+    float n = bfv(orc_bf16_value(x[i]) * rho);
+    u[i] = bfv(n * orc_bf16_value(w[i]));
+  }
+  for (int64_t i = 0; i < Dh / 2; ++i) {
+    float a = u[2 * i], b = u[2 * i + 1];
+    o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);
+    o[2 * i + 1] = orc_bf16_round(a * z[i] + b * c[i]);
+  }
+}
+
+static void qkv_stream(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_t out_ts,
+                       int64_t out_bs, const orc_qkv_stream *st, int64_t joint_first,
+                       const float *cos_t, const float *sin_t, int64_t batch, int64_t heads,
+                       int64_t Dh, float eps) {
+  int64_t half = Dh / 2;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t s = 0; s < st->tokens; ++s) {
+      int64_t jt = joint_first + s;
+      const float *c = cos_t + jt * half;
+      const float *z = sin_t + jt * half;
+      int64_t src = b * st->batch_stride + s * st->tok_stride;
+      int64_t dst = b * out_bs + jt * out_ts;
+      for (int64_t h = 0; h < heads; ++h) {
+        orc_qk_head(st->q + src + h * Dh, st->q_weight, c, z, Dh, eps, q_out + dst + h * Dh);
+        orc_qk_head(st->k + src + h * Dh, st->k_weight, c, z, Dh, eps, k_out + dst + h * Dh);
+        memcpy(v_out + dst + h * Dh, st->v + src + h * Dh, sizeof(uint16_t) * (size_t)Dh);
+      }
+    }
+}
+
+/* Text tokens occupy joint rows [0, S_txt), image tokens [S_txt, S_txt+S_img). */
+int orc_qk_norm_rope(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_t out_tok_stride,
+                     int64_t out_batch_stride, const orc_qkv_stream *txt,
+                     const orc_qkv_stream *img, const float *cos_t, const float *sin_t,
+                     int64_t batch, int64_t heads, int64_t head_dim, float eps) {
+  if (head_dim < 8 || head_dim > 512 || head_dim % 8) return 1;
+  int64_t lanes = head_dim / 8;
+  if (lanes & (lanes - 1)) return 1;
+  if (txt && txt->tokens > 0)
+    qkv_stream(q_out, k_out, v_out, out_tok_stride, out_batch_stride, txt, 0, cos_t, sin_t,
+               batch, heads, head_dim, eps);
+  if (img && img->tokens > 0)
+    qkv_stream(q_out, k_out, v_out, out_tok_stride, out_batch_stride, img,
+               txt ? txt->tokens : 0, cos_t, sin_t, batch, heads, head_dim, eps);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Array helpers for exhaustive tests                                        */
+/* ------------------------------------------------------------------------- */
+
+void orc_bf16_round_array(const float *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(in[i]);
+}
+
+/* Rounds every binary32 whose bit pattern lies in [first, first + n) and
+ * returns them in out (used to sweep all 2^32 inputs in slices). */
+void orc_bf16_round_bits_range(uint32_t first, int64_t n, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(bits_f32(first + (uint32_t)i));
+}
+
+void orc_tanh_array(const uint16_t *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_tanh(in[i]);
+}
+
+void orc_one_plus_array(const uint16_t *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_one_plus(in[i]);
+}
+
+void orc_rms_rstd_array(const uint16_t *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_rms_rstd(in[i]);
+}
+
+/* tanh of every bf16 input in long double, for the oracle's own pin: writes
+ * the correctly rounded bf16 and the distance of the long double value from
+ * the nearest bf16 rounding boundary, relative to its magnitude. */
+void orc_tanh_check_ld(const uint16_t *in, uint16_t *out, double *tie_margin, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    float v = orc_bf16_value(in[i]);
+    if (isnan(v) || isinf(v) || v == 0.0f) {
+      out[i] = isnan(v) ? (uint16_t)(in[i] | 0x0040u) : orc_tanh(in[i]);
+      tie_margin[i] = 1.0;
+      continue;
+    }
+    long double t = tanhl((long double)v);
+    long double a = fabsl(t);
+    int e;
+    frexpl(a, &e);
+    int ulp_exp = e - 8;
+    if (ulp_exp < -133) ulp_exp = -133;
+    long double q = ldexpl(a, -ulp_exp);
+    long double fl = floorl(q);
+    long double frac = q - fl;                     /* position inside the ulp */
+    long double dist = fabsl(frac - 0.5L);         /* distance to the midpoint */
+    tie_margin[i] = (double)(ldexpl(dist, ulp_exp) / a);
+    long double r = frac > 0.5L ? fl + 1 : (frac < 0.5L ? fl : (fmodl(fl, 2.0L) == 0 ? fl : fl + 1));
+    out[i] = orc_bf16_round_f64((double)(copysignl(ldexpl(r, ulp_exp), t)));
+  }
+}
