@@ -1,0 +1,269 @@
+"""Benchmark of the BF16 DiT row epilogues on one MI355X.
+
+One step = one pass of the whole epilogue path over one Qwen-Image 1024x1024
+DiT block (CFG batch 2: 4096 image + 512 text tokens, hidden 3072, 24 heads
+of 128), all in LOSSLESS mode:
+
+  LN + AdaLN modulate       x [9216, 3072], per-batch scale/shift [2, 3072]
+  RMSNorm-scale             x [9216, 3072], weight [3072], per-batch scale
+  RMSNorm-tanh-residual     x, residual [9216, 3072], per-batch gate
+  residual gate-add         residual, y [9216, 3072], per-batch gate
+  Q/K RMSNorm + RoPE + joint QKV   merged QKV [2, 4096|512, 9216] -> 3 x [2, 4608, 24, 128]
+
+Inputs are resident in HBM before timing.  Two complete buffer sets are
+alternated step by step so that every kernel's operands were last touched
+about 1.4 GB of traffic earlier: the 256 MB Infinity Cache cannot serve them.
+Per-kernel durations come from HIP events recorded on the launch stream.
+
+value = algorithmic bytes of one step / time per step (GB/s, whole job).
+The roofline object reports LN + AdaLN modulate, the kernel the metric names.
+The CPU baseline runs the oracle (plain C, one thread) over one full step on
+the host and also compares its outputs with the GPU's, bit for bit.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for fused LN+AdaLN modulate; bit-exact pass"
+PEAK_GBS = 8000.0
+
+B, S_IMG, S_TXT, D, H, DH = 2, 4096, 512, 3072, 24, 128
+ROWS = B * (S_IMG + S_TXT)
+EPS = 1e-6
+
+# Algorithmic bytes per call: every operand read once, every output written once.
+BYTES = {
+    "ln_modulate": 2 * ROWS * D * 2 + 2 * B * D * 2,                 # x, out; scale, shift
+    "rmsnorm_scale": 2 * ROWS * D * 2 + D * 2 + B * D * 2,           # x, out; w; scale
+    "rmsnorm_tanh_residual": 3 * ROWS * D * 2 + D * 2 + B * D * 2,   # x, res, out; w; gate
+    "residual_gate_add": 3 * ROWS * D * 2 + B * D * 2,               # res, y, out; gate
+    "qk_norm_rope": 2 * 3 * ROWS * H * DH * 2 + 4 * DH * 2 + 2 * (S_IMG + S_TXT) * (DH // 2) * 4,
+}
+KERNELS = list(BYTES)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "modulation_bf16_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_qwen1024.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs():
+    from modulation_bf16_row_amd import synth
+    blk = synth.qwen_image_block()
+    qkv = synth.qwen_image_qkv()
+    blk["y"] = synth.normal_bf16((ROWS, D), 1.0, 2007)
+    return blk, qkv
+
+
+def to_dev(h, torch):
+    return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class BufferSet:
+    def __init__(self, blk, qkv, torch):
+        self.x = to_dev(blk["x"], torch)
+        self.res = to_dev(blk["residual"], torch)
+        self.y = to_dev(blk["y"], torch)
+        self.scale = to_dev(blk["scale"], torch)
+        self.shift = to_dev(blk["shift"], torch)
+        self.gate = to_dev(blk["gate"], torch)
+        self.scale2 = to_dev(blk["scale2"], torch)
+        self.w = to_dev(blk["weight"], torch)
+        self.out = {k: torch.empty((ROWS, D), dtype=torch.bfloat16, device="cuda")
+                    for k in KERNELS[:4]}
+        img = to_dev(qkv["img_qkv"], torch)
+        txt = to_dev(qkv["txt_qkv"], torch)
+        self._keep = (img, txt)
+
+        def views(a):
+            return [a[:, :, i * H * DH:(i + 1) * H * DH].view(a.shape[0], a.shape[1], H, DH)
+                    for i in range(3)]
+        tq, tk, tv = views(txt)
+        iq, ik, iv = views(img)
+        self.txt = dict(q=tq, k=tk, v=tv, q_weight=to_dev(qkv["txt_q_weight"], torch),
+                        k_weight=to_dev(qkv["txt_k_weight"], torch))
+        self.img = dict(q=iq, k=ik, v=iv, q_weight=to_dev(qkv["img_q_weight"], torch),
+                        k_weight=to_dev(qkv["img_k_weight"], torch))
+        self.cos = torch.from_numpy(qkv["cos"]).cuda()
+        self.sin = torch.from_numpy(qkv["sin"]).cuda()
+        self.qkv_out = tuple(torch.empty((B, S_TXT + S_IMG, H, DH), dtype=torch.bfloat16,
+                                         device="cuda") for _ in range(3))
+
+
+def run_step(m, s, mode, ev=None):
+    """Launches the five epilogues; ev[k] = (start, end) events per kernel."""
+    def rec(k, i):
+        if ev is not None:
+            ev[k][i].record()
+    rec("ln_modulate", 0)
+    m.dit_ln_modulate(s.x, s.scale, s.shift, EPS, mode, out=s.out["ln_modulate"])
+    rec("ln_modulate", 1)
+    rec("rmsnorm_scale", 0)
+    m.dit_rmsnorm_scale(s.x, s.w, s.scale2, EPS, mode, out=s.out["rmsnorm_scale"])
+    rec("rmsnorm_scale", 1)
+    rec("rmsnorm_tanh_residual", 0)
+    m.dit_rmsnorm_tanh_residual(s.x, s.res, s.w, s.gate, EPS, mode,
+                                out=s.out["rmsnorm_tanh_residual"])
+    rec("rmsnorm_tanh_residual", 1)
+    rec("residual_gate_add", 0)
+    m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.out["residual_gate_add"])
+    rec("residual_gate_add", 1)
+    rec("qk_norm_rope", 0)
+    m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode, out=s.qkv_out)
+    rec("qk_norm_rope", 1)
+
+
+def cpu_baseline(blk, qkv, gpu_out):
+    """The oracle over one full step on the host (single thread), timed, and
+    its outputs compared with the GPU's bit for bit."""
+    import oracle
+    t_ops = {}
+    refs = {}
+    t0 = time.perf_counter()
+    refs["ln_modulate"] = oracle.ln_modulate(blk["x"], blk["scale"], blk["shift"], EPS)
+    t_ops["ln_modulate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    refs["rmsnorm_scale"] = oracle.rmsnorm_scale(blk["x"], blk["weight"], blk["scale2"], EPS)
+    t_ops["rmsnorm_scale"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    refs["rmsnorm_tanh_residual"] = oracle.rmsnorm_tanh_residual(
+        blk["x"], blk["residual"], blk["weight"], blk["gate"], EPS)
+    t_ops["rmsnorm_tanh_residual"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    refs["residual_gate_add"] = oracle.residual_gate_add(blk["residual"], blk["y"], blk["gate"])
+    t_ops["residual_gate_add"] = time.perf_counter() - t0
+
+    def views(a):
+        return [a[:, :, i * H * DH:(i + 1) * H * DH].reshape(a.shape[0], a.shape[1], H, DH)
+                for i in range(3)]
+    tq, tk, tv = views(qkv["txt_qkv"])
+    iq, ik, iv = views(qkv["img_qkv"])
+    t0 = time.perf_counter()
+    refs["qk_norm_rope"] = oracle.qk_norm_rope(
+        dict(q=tq, k=tk, v=tv, q_weight=qkv["txt_q_weight"], k_weight=qkv["txt_k_weight"]),
+        dict(q=iq, k=ik, v=iv, q_weight=qkv["img_q_weight"], k_weight=qkv["img_k_weight"]),
+        qkv["cos"], qkv["sin"], EPS)
+    t_ops["qk_norm_rope"] = time.perf_counter() - t0
+    total_t = sum(t_ops.values())
+    exact = {}
+    for k in KERNELS[:4]:
+        exact[k] = bool(np.array_equal(gpu_out[k], refs[k]))
+    exact["qk_norm_rope"] = all(np.array_equal(g, r) for g, r in zip(gpu_out["qk_norm_rope"],
+                                                                     refs["qk_norm_rope"]))
+    value = sum(BYTES.values()) / total_t / 1e9
+    return dict(value=round(value, 4), unit="GB/s", cores=1, kind="oracle",
+                sample="one full step (all five epilogues at the Qwen-Image 1024x1024 shapes), "
+                       "single-threaded oracle, %.1f s" % total_t,
+                seconds_per_op={k: round(v, 3) for k, v in t_ops.items()}), exact
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="lossless", choices=["lossless", "fast"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the epilogues shard by rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import modulation_bf16_row_amd as m
+    m.lib()
+    torch.cuda.init()
+    blk, qkv = make_inputs()
+    sets = [BufferSet(blk, qkv, torch), BufferSet(blk, qkv, torch)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_step(m, sets[i % 2], args.mode)
+    torch.cuda.synchronize()
+
+    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for _ in range(args.steps)] for k in KERNELS}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run_step(m, sets[i % 2], args.mode, {k: ev[k][i] for k in KERNELS})
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    k_us = {k: 1000.0 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev[k]]))
+            for k in KERNELS}
+
+    step_bytes = sum(BYTES.values())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    per_kernel = {k: dict(us=round(k_us[k], 2), bytes=BYTES[k],
+                          gbs=round(BYTES[k] / (k_us[k] * 1e-6) / 1e9, 1),
+                          frac=round(BYTES[k] / (k_us[k] * 1e-6) / 1e9 / PEAK_GBS, 4))
+                  for k in KERNELS}
+    dom = "ln_modulate"
+    achieved = per_kernel[dom]["gbs"]
+    roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBS, 4), traffic=read_traffic(dom),
+                    kernel=dom, bytes_per_launch=BYTES[dom], launch_us=per_kernel[dom]["us"])
+
+    result = dict(
+        metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(ms_step, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="Qwen-Image 1024x1024 DiT block epilogues (LN+AdaLN modulate, "
+                             "RMSNorm-scale, RMSNorm-tanh-residual, residual gate-add, "
+                             "Q/K RMSNorm+RoPE+joint QKV)",
+                    batch=B, tokens=S_IMG + S_TXT, hidden=D, heads=H, head_dim=DH,
+                    mode=args.mode, step_bytes=step_bytes, host_wall_ms_per_step=round(
+                        1000 * wall / args.steps, 4)),
+        roofline=roofline, kernels=per_kernel,
+    )
+    if not args.no_cpu:
+        gpu_out = {k: sets[0].out[k].cpu().view(torch.int16).numpy().view(np.uint16)
+                   for k in KERNELS[:4]}
+        gpu_out["qk_norm_rope"] = [t.cpu().view(torch.int16).numpy().view(np.uint16)
+                                   for t in sets[0].qkv_out]
+        base, exact = cpu_baseline(blk, qkv, gpu_out)
+        result["cpu_baseline"] = base
+        result["bit_exact_full_step"] = exact if args.mode == "lossless" else None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,52 @@
+/*
+ * dit_probe.h -- entry points that run the epilogue kernels' own device
+ * primitives over caller arrays.  They exist so that each primitive can be
+ * checked exhaustively (all 65536 bf16 inputs, all 2^32 binary32 inputs)
+ * against an independent CPU reference; they are not needed to use the
+ * epilogues.  Conventions (ownership, asynchrony, status codes, thread-local
+ * reason) are those of dit.h.  n == 0 is a valid empty call.
+ */
+#ifndef DIT_PROBE_H
+#define DIT_PROBE_H
+
+#include "dit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* out[i] = bf16 bits of in[i] rounded to nearest even (the kernels' packer). */
+dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t stream);
+
+typedef enum {
+  DIT_PROBE_ONE_PLUS = 0,  /* bf(1 + s)                                    */
+  DIT_PROBE_TANH = 1,      /* bf16 tanh of a bf16 gate (mode-dependent)     */
+  DIT_PROBE_RMS_RSTD = 2   /* bf(1 / sqrt(v)) of the RMSNorm chain (mode)   */
+} dit_probe_unary_t;
+
+/* out[i] = op(in[i]) on bf16 bit patterns. */
+dit_status_t dit_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
+                             hipStream_t stream);
+
+typedef enum {
+  DIT_PROBE_DIV = 0,    /* a / b                         */
+  DIT_PROBE_SQRT = 1,   /* sqrt(a)                       */
+  DIT_PROBE_RSQRT = 2   /* 1 / sqrt(a) as the norms use it (mode) */
+} dit_probe_f32_t;
+
+/* out[i] = op(a[i], b[i]) in binary32; b is ignored (may be NULL) unless op
+ * is DIT_PROBE_DIV. */
+dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, int64_t n,
+                           int mode, hipStream_t stream);
+
+/* head == 0: out[r] = R(dim) sum of t[r*dim .. r*dim+dim) (dim <= 8192,
+ *            dim % 8 == 0), one wave per row.
+ * head == 1: out[g] = 16-lane head sum of t[g*128 .. g*128+128); dim must be
+ *            128. */
+dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_PROBE_H */

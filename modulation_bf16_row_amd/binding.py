@@ -1,0 +1,320 @@
+"""ctypes binding of libdit.so (argument marshalling only).
+
+Each ``dit_*`` function takes torch tensors on a ROCm device, checks dtype,
+device and layout, folds the leading dimensions into flat rows, and calls
+the C entry point of the same name on the current torch stream.  Every step
+of the computation runs in the HIP kernels; there is no CPU or PyTorch
+fallback.  A problem outside the fast path raises ``DitUnsupported`` (the
+caller decides what to run instead); bad arguments raise ``DitInvalid``.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdit.so")
+
+LOSSLESS = 0
+FAST = 1
+_MODES = {"lossless": LOSSLESS, "fast": FAST, LOSSLESS: LOSSLESS, FAST: FAST}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_int = ctypes.c_int
+
+
+class DitError(RuntimeError):
+    pass
+
+
+class DitUnsupported(DitError):
+    pass
+
+
+class DitInvalid(DitError):
+    pass
+
+
+class DitHipError(DitError):
+    pass
+
+
+class QkvStream(ctypes.Structure):
+    """dit_qkv_stream_t"""
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("tok_stride", _i64),
+                ("batch_stride", _i64), ("q_weight", _vp), ("k_weight", _vp), ("tokens", _i64)]
+
+
+_lib = None
+
+# name -> argtypes of every exported function
+SIGNATURES = {
+    "dit_abi_version": [],
+    "dit_status_string": [_int],
+    "dit_status_reason": [],
+    "dit_ln_modulate": [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp],
+    "dit_rmsnorm_scale": [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int,
+                          _vp],
+    "dit_rmsnorm_tanh_residual": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+                                  _i64, _f32, _int, _vp],
+    "dit_residual_gate_add": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int,
+                              _vp],
+    "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
+                         ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
+    "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
+    "dit_probe_unary": [_int, _vp, _vp, _i64, _int, _vp],
+    "dit_probe_f32": [_int, _vp, _vp, _vp, _i64, _int, _vp],
+    "dit_probe_row_sum": [_vp, _vp, _i64, _i64, _int, _vp],
+}
+
+
+def lib():
+    """The loaded libdit.so.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m modulation_bf16_row_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = _int
+        h.dit_status_string.restype = ctypes.c_char_p
+        h.dit_status_reason.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def _check(status):
+    if status == 0:
+        return
+    reason = lib().dit_status_reason().decode()
+    if status == 1:
+        raise DitUnsupported(reason)
+    if status == 2:
+        raise DitInvalid(reason)
+    raise DitHipError(reason)
+
+
+def _mode(mode):
+    try:
+        return _MODES[mode]
+    except KeyError:
+        raise DitInvalid(f"unknown mode {mode!r}") from None
+
+
+def _stream(t):
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _flat_rows(t, name):
+    """(rows, row_stride) of a [..., dim] tensor whose outer dimensions fold
+    into one uniform row stride (the flat-row-stride rule)."""
+    if t.dtype != torch.bfloat16:
+        raise DitUnsupported(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise DitUnsupported(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dim() == 0:
+        raise DitUnsupported(f"{name} must have a last dimension")
+    dim = t.shape[-1]
+    if t.dim() == 1:
+        return 1, dim
+    if t.stride(-1) != 1 and dim > 1:
+        raise DitUnsupported(f"{name}: last dimension is not contiguous")
+    rs = t.stride(-2)
+    expected = rs * t.shape[-2]
+    for d in range(t.dim() - 3, -1, -1):
+        if t.shape[d] != 1 and t.stride(d) != expected:
+            raise DitUnsupported(f"{name}: outer dimensions do not fold into flat rows")
+        expected *= t.shape[d]
+    rows = t.numel() // dim if dim else 0
+    return rows, rs
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t.device != dev:
+            raise DitUnsupported("all tensors must be on the same device")
+
+
+def _out_like(x, out):
+    if out is None:
+        return torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    if out.shape != x.shape:
+        raise DitInvalid(f"out has shape {tuple(out.shape)}, expected {tuple(x.shape)}")
+    return out
+
+
+def _mod_rows(a, b, dim, names):
+    ra, sa = _flat_rows(a, names[0])
+    if a.shape[-1] != dim:
+        raise DitInvalid(f"{names[0]} last dimension {a.shape[-1]} != {dim}")
+    if b is not None:
+        rb, sb = _flat_rows(b, names[1])
+        if b.shape[-1] != dim or rb != ra:
+            raise DitInvalid(f"{names[1]} shape does not match {names[0]}")
+        if sb != sa and ra > 1:
+            raise DitUnsupported(f"{names[0]} and {names[1]} must share one row stride")
+    return ra, sa
+
+
+def dit_ln_modulate(x, scale, shift, eps=1e-6, mode="lossless", out=None):
+    """LN(x) * (1 + scale) + shift with the lossless rounding contract."""
+    _same_device(x, scale, shift)
+    rows, x_rs = _flat_rows(x, "x")
+    dim = x.shape[-1]
+    mrows, mrs = _mod_rows(scale, shift, dim, ("scale", "shift"))
+    out = _out_like(x, out)
+    _same_device(x, out)
+    _, o_rs = _flat_rows(out, "out")
+    _check(lib().dit_ln_modulate(out.data_ptr(), o_rs, x.data_ptr(), x_rs, scale.data_ptr(),
+                                 shift.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
+                                 _stream(x)))
+    return out
+
+
+def dit_rmsnorm_scale(x, weight, scale, eps=1e-6, mode="lossless", out=None):
+    _same_device(x, weight, scale)
+    rows, x_rs = _flat_rows(x, "x")
+    dim = x.shape[-1]
+    if weight.dtype != torch.bfloat16 or weight.numel() != dim or not weight.is_contiguous():
+        raise DitUnsupported("weight must be a contiguous bfloat16 tensor of dim elements")
+    mrows, mrs = _mod_rows(scale, None, dim, ("scale",))
+    out = _out_like(x, out)
+    _same_device(x, out)
+    _, o_rs = _flat_rows(out, "out")
+    _check(lib().dit_rmsnorm_scale(out.data_ptr(), o_rs, x.data_ptr(), x_rs, weight.data_ptr(),
+                                   scale.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
+                                   _stream(x)))
+    return out
+
+
+def dit_rmsnorm_tanh_residual(x, residual, weight, gate, eps=1e-6, mode="lossless", out=None):
+    _same_device(x, residual, weight, gate)
+    rows, x_rs = _flat_rows(x, "x")
+    dim = x.shape[-1]
+    rrows, r_rs = _flat_rows(residual, "residual")
+    if residual.shape != x.shape:
+        raise DitInvalid("residual must have the shape of x")
+    if weight.dtype != torch.bfloat16 or weight.numel() != dim or not weight.is_contiguous():
+        raise DitUnsupported("weight must be a contiguous bfloat16 tensor of dim elements")
+    mrows, mrs = _mod_rows(gate, None, dim, ("gate",))
+    out = _out_like(x, out)
+    _same_device(x, out)
+    _, o_rs = _flat_rows(out, "out")
+    _check(lib().dit_rmsnorm_tanh_residual(out.data_ptr(), o_rs, x.data_ptr(), x_rs,
+                                           residual.data_ptr(), r_rs, weight.data_ptr(),
+                                           gate.data_ptr(), mrs, mrows, rows, dim, eps,
+                                           _mode(mode), _stream(x)))
+    return out
+
+
+def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None):
+    _same_device(residual, y, gate)
+    rows, r_rs = _flat_rows(residual, "residual")
+    dim = residual.shape[-1]
+    if y.shape != residual.shape:
+        raise DitInvalid("y must have the shape of residual")
+    _, y_rs = _flat_rows(y, "y")
+    mrows, mrs = _mod_rows(gate, None, dim, ("gate",))
+    out = _out_like(residual, out)
+    _same_device(residual, out)
+    _, o_rs = _flat_rows(out, "out")
+    _check(lib().dit_residual_gate_add(out.data_ptr(), o_rs, residual.data_ptr(), r_rs,
+                                       y.data_ptr(), y_rs, gate.data_ptr(), mrs, mrows, rows,
+                                       dim, _mode(mode), _stream(residual)))
+    return out
+
+
+def _qkv_stream(st):
+    """st: dict with q, k, v ([B, S, H, Dh] views sharing strides) and q_weight,
+    k_weight ([Dh]); None means no tokens."""
+    if st is None:
+        return QkvStream(), (0, 0, 0, 0)
+    q, k, v = st["q"], st["k"], st["v"]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise DitUnsupported(f"{n} must be a bfloat16 [B, S, H, Dh] view")
+        if t.stride(3) != 1 or t.stride(2) != t.shape[3]:
+            raise DitUnsupported(f"{n}: heads must be packed (head stride Dh, element stride 1)")
+    if not (q.stride() == k.stride() == v.stride() and q.shape == k.shape == v.shape):
+        raise DitUnsupported("q, k, v of one stream must share shape and strides")
+    for w, n in ((st["q_weight"], "q_weight"), (st["k_weight"], "k_weight")):
+        if w.dtype != torch.bfloat16 or not w.is_contiguous() or w.numel() != q.shape[3]:
+            raise DitUnsupported(f"{n} must be a contiguous bfloat16 [Dh] tensor")
+    s = QkvStream(q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), tok_stride=q.stride(1),
+                  batch_stride=q.stride(0), q_weight=st["q_weight"].data_ptr(),
+                  k_weight=st["k_weight"].data_ptr(), tokens=q.shape[1])
+    return s, tuple(q.shape)
+
+
+def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None):
+    """Q/K RMSNorm + interleaved RoPE + V copy into joint [B, S_txt + S_img, H, Dh]
+    outputs (text tokens first).  ``out`` may be a (q, k, v) triple of views
+    sharing token and batch strides."""
+    ts, tshape = _qkv_stream(txt)
+    is_, ishape = _qkv_stream(img)
+    ref = img["q"] if img is not None else txt["q"]
+    B, _, H, Dh = ref.shape
+    s_total = ts.tokens + is_.tokens
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32 or not cos.is_contiguous() \
+            or not sin.is_contiguous():
+        raise DitUnsupported("cos and sin must be contiguous float32 tensors")
+    if cos.shape != (s_total, Dh // 2) or sin.shape != (s_total, Dh // 2):
+        raise DitInvalid(f"cos/sin must be [{s_total}, {Dh // 2}]")
+    for sh in (tshape, ishape):
+        if sh[0] and (sh[0] != B or sh[2] != H or sh[3] != Dh):
+            raise DitInvalid("text and image streams must agree on batch, heads and head_dim")
+    if out is None:
+        out = tuple(torch.empty((B, s_total, H, Dh), dtype=torch.bfloat16, device=ref.device)
+                    for _ in range(3))
+    qo, ko, vo = out
+    for t in out:
+        if t.shape != (B, s_total, H, Dh) or t.dtype != torch.bfloat16:
+            raise DitInvalid("outputs must be bfloat16 [B, S_txt + S_img, H, Dh]")
+        if t.stride(3) != 1 or t.stride(2) != Dh or t.stride() != qo.stride():
+            raise DitUnsupported("outputs must share strides with packed heads")
+    _check(lib().dit_qk_norm_rope(qo.data_ptr(), ko.data_ptr(), vo.data_ptr(), qo.stride(1),
+                                  qo.stride(0), ctypes.byref(ts), ctypes.byref(is_),
+                                  cos.data_ptr(), sin.data_ptr(), B, H, Dh, eps, _mode(mode),
+                                  _stream(ref)))
+    return out
+
+
+# --- probes of the device primitives ---------------------------------------------------
+
+def dit_probe_bf16_round(x_f32, out=None):
+    if out is None:
+        out = torch.empty(x_f32.shape, dtype=torch.int16, device=x_f32.device)
+    _check(lib().dit_probe_bf16_round(out.data_ptr(), x_f32.data_ptr(), x_f32.numel(),
+                                      _stream(x_f32)))
+    return out
+
+
+def dit_probe_unary(op, h_i16, mode="lossless"):
+    out = torch.empty_like(h_i16)
+    _check(lib().dit_probe_unary(op, out.data_ptr(), h_i16.data_ptr(), h_i16.numel(),
+                                 _mode(mode), _stream(h_i16)))
+    return out
+
+
+def dit_probe_f32(op, a, b=None, mode="lossless"):
+    out = torch.empty_like(a)
+    _check(lib().dit_probe_f32(op, out.data_ptr(), a.data_ptr(),
+                               b.data_ptr() if b is not None else None, a.numel(), _mode(mode),
+                               _stream(a)))
+    return out
+
+
+def dit_probe_row_sum(t, head=False):
+    """t: float32 [rows, dim] contiguous -> float32 [rows] (head: [groups])."""
+    rows, dim = t.shape
+    out = torch.empty(rows, dtype=torch.float32, device=t.device)
+    _check(lib().dit_probe_row_sum(out.data_ptr(), t.data_ptr(), rows, dim, int(head),
+                                   _stream(t)))
+    return out

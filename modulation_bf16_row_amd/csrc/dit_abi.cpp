@@ -1,0 +1,393 @@
+// dit_abi.cpp -- extern "C" entry points of the epilogue library: argument
+// guards (pure host code, run before any HIP call) and dispatch to the
+// kernel launchers.
+//
+// The guard rules follow the eligibility checks the pages describe for the
+// shared native-bf16 kernels (page "#34085 [diffusion] Clean up kernels and
+// shared fast paths", sections "实现拆解" and "关键源码片段": same device, all
+// bf16, hidden size at most 8192, non-empty, weight shape and contiguity,
+// flat row stride, rows divisible by modulation rows).  Where those return
+// "no fast path" to the caller, this library returns DIT_ERR_UNSUPPORTED
+// with a reason -- never a silent fallback.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dit.h"
+#include "dit_launch.hpp"
+#include "dit_probe.h"
+
+namespace {
+
+thread_local const char *g_reason = "";
+
+dit_status_t fail(dit_status_t s, const char *why) {
+  g_reason = why;
+  return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A set of byte segments [base + i*step, base + i*step + len), i < count.
+struct Span {
+  uintptr_t base;
+  int64_t step;
+  int64_t count;
+  int64_t len;
+};
+
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+  int64_t q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// True if some byte belongs to both spans.  Exact when both have the same
+// step (or one has a single segment); otherwise compares the hulls, which
+// may report an overlap that the segments avoid (the safe direction).
+bool spans_overlap(Span a, Span b) {
+  if (a.count <= 0 || b.count <= 0 || a.len <= 0 || b.len <= 0) return false;
+  if (a.count == 1 || a.step <= 0) { a.count = 1; a.step = b.step; }
+  if (b.count == 1 || b.step <= 0) { b.count = 1; b.step = a.step; }
+  const uintptr_t a_end = a.base + (uintptr_t)((a.count - 1) * a.step + a.len);
+  const uintptr_t b_end = b.base + (uintptr_t)((b.count - 1) * b.step + b.len);
+  if (a_end <= b.base || b_end <= a.base) return false;
+  if (a.step != b.step || a.step <= 0) return true;
+  // overlap iff -a.len < delta + m*step < b.len for some m in
+  // [-(a.count-1), b.count-1], delta = b.base - a.base
+  const int64_t delta = (int64_t)(b.base - a.base);
+  int64_t m = floor_div(-a.len - delta, a.step) + 1;
+  m = std::max(m, -(a.count - 1));
+  if (m > b.count - 1) return false;
+  return delta + m * a.step < b.len;
+}
+
+Span rows_span(const void *p, int64_t rs, int64_t rows, int64_t dim) {
+  return Span{reinterpret_cast<uintptr_t>(p), rs * 2, rows, dim * 2};
+}
+
+// Common checks of a row tensor argument; returns DIT_OK or the failure.
+dit_status_t check_rows(const void *p, int64_t rs, int64_t rows, int64_t dim, const char *null_msg,
+                        const char *stride_msg) {
+  if (!p) return fail(DIT_ERR_INVALID, null_msg);
+  if (rs < 0) return fail(DIT_ERR_INVALID, stride_msg);
+  if (rows > 1 && (rs < dim || rs % 8 != 0)) return fail(DIT_ERR_UNSUPPORTED, stride_msg);
+  if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "tensor pointer is not 16-byte aligned");
+  return DIT_OK;
+}
+
+// Shared checks of the four row ops.  `ins` are row inputs that `out` may
+// equal exactly; `consts` are inputs it must not touch at all.
+struct RowProblem {
+  int64_t rows, dim, mod_rows;
+  int mode;
+};
+
+dit_status_t check_shape(const RowProblem &p, bool has_mode) {
+  if (has_mode && p.mode != DIT_MODE_LOSSLESS && p.mode != DIT_MODE_FAST)
+    return fail(DIT_ERR_INVALID, "unknown mode");
+  if (p.rows < 0 || p.dim < 0 || p.mod_rows < 0)
+    return fail(DIT_ERR_INVALID, "negative size");
+  if (p.rows == 0) return DIT_OK;
+  if (p.dim == 0) return fail(DIT_ERR_UNSUPPORTED, "dim == 0");
+  if (p.dim > DIT_MAX_DIM) return fail(DIT_ERR_UNSUPPORTED, "dim > 8192");
+  if (p.dim % 8 != 0) return fail(DIT_ERR_UNSUPPORTED, "dim % 8 != 0");
+  if (p.mod_rows == 0) return fail(DIT_ERR_INVALID, "mod_rows == 0 with rows > 0");
+  if (p.rows % p.mod_rows != 0) return fail(DIT_ERR_UNSUPPORTED, "rows % mod_rows != 0");
+  if ((p.rows + 3) / 4 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
+  return DIT_OK;
+}
+
+dit_status_t check_out_alias(const Span &out, const Span *ins, int n_ins, const Span *consts,
+                             int n_consts) {
+  for (int i = 0; i < n_ins; ++i) {
+    const bool same = ins[i].base == out.base && (ins[i].step == out.step || out.count == 1);
+    if (!same && spans_overlap(out, ins[i]))
+      return fail(DIT_ERR_INVALID, "output partially overlaps a row input");
+  }
+  for (int i = 0; i < n_consts; ++i)
+    if (spans_overlap(out, consts[i]))
+      return fail(DIT_ERR_INVALID, "output overlaps a modulation or weight tensor");
+  return DIT_OK;
+}
+
+dit_status_t hip_status(hipError_t e) {
+  if (e != hipSuccess) return fail(DIT_ERR_HIP, hipGetErrorString(e));
+  return DIT_OK;
+}
+
+#define DIT_TRY(expr)                    \
+  do {                                   \
+    dit_status_t _s = (expr);            \
+    if (_s != DIT_OK) return _s;         \
+  } while (0)
+
+const uint16_t *u16(const void *p) { return static_cast<const uint16_t *>(p); }
+
+}  // namespace
+
+extern "C" {
+
+int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+const char *dit_status_string(dit_status_t s) {
+  switch (s) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED";
+    case DIT_ERR_INVALID: return "DIT_ERR_INVALID";
+    case DIT_ERR_HIP: return "DIT_ERR_HIP";
+  }
+  return "DIT_STATUS_UNKNOWN";
+}
+
+const char *dit_status_reason(void) { return g_reason; }
+
+dit_status_t dit_ln_modulate(void *out, int64_t out_rs, const void *x, int64_t x_rs,
+                             const void *scale, const void *shift, int64_t mod_rs,
+                             int64_t mod_rows, int64_t rows, int64_t dim, float eps, int mode,
+                             hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(x, x_rs, rows, dim, "x is NULL", "bad x row stride"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(shift, mod_rs, mod_rows, dim, "shift is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(x, x_rs, rows, dim)};
+  const Span cs[] = {rows_span(scale, mod_rs, mod_rows, dim),
+                     rows_span(shift, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 1, cs, 2));
+  dit::LnModArgs a{static_cast<uint16_t *>(out), u16(x), u16(scale), u16(shift), out_rs, x_rs,
+                   mod_rs, rows, dim, rows / mod_rows, eps};
+  return hip_status(dit::launch_ln_modulate(a, mode, stream));
+}
+
+dit_status_t dit_rmsnorm_scale(void *out, int64_t out_rs, const void *x, int64_t x_rs,
+                               const void *weight, const void *scale, int64_t mod_rs,
+                               int64_t mod_rows, int64_t rows, int64_t dim, float eps, int mode,
+                               hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(x, x_rs, rows, dim, "x is NULL", "bad x row stride"));
+  DIT_TRY(check_rows(weight, dim, 1, dim, "weight is NULL", "bad weight"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(x, x_rs, rows, dim)};
+  const Span cs[] = {rows_span(weight, dim, 1, dim), rows_span(scale, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 1, cs, 2));
+  dit::RmsScaleArgs a{static_cast<uint16_t *>(out), u16(x), u16(weight), u16(scale), out_rs,
+                      x_rs, mod_rs, rows, dim, rows / mod_rows, eps};
+  return hip_status(dit::launch_rmsnorm_scale(a, mode, stream));
+}
+
+dit_status_t dit_rmsnorm_tanh_residual(void *out, int64_t out_rs, const void *x, int64_t x_rs,
+                                       const void *residual, int64_t res_rs, const void *weight,
+                                       const void *gate, int64_t mod_rs, int64_t mod_rows,
+                                       int64_t rows, int64_t dim, float eps, int mode,
+                                       hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(x, x_rs, rows, dim, "x is NULL", "bad x row stride"));
+  DIT_TRY(check_rows(residual, res_rs, rows, dim, "residual is NULL", "bad residual row stride"));
+  DIT_TRY(check_rows(weight, dim, 1, dim, "weight is NULL", "bad weight"));
+  DIT_TRY(check_rows(gate, mod_rs, mod_rows, dim, "gate is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(x, x_rs, rows, dim), rows_span(residual, res_rs, rows, dim)};
+  const Span cs[] = {rows_span(weight, dim, 1, dim), rows_span(gate, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 2, cs, 2));
+  dit::RmsTanhArgs a{static_cast<uint16_t *>(out), u16(x), u16(residual), u16(weight),
+                     u16(gate), out_rs, x_rs, res_rs, mod_rs, rows, dim, rows / mod_rows, eps};
+  return hip_status(dit::launch_rmsnorm_tanh_residual(a, mode, stream));
+}
+
+dit_status_t dit_residual_gate_add(void *out, int64_t out_rs, const void *residual,
+                                   int64_t res_rs, const void *y, int64_t y_rs, const void *gate,
+                                   int64_t mod_rs, int64_t mod_rows, int64_t rows, int64_t dim,
+                                   int mode, hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(residual, res_rs, rows, dim, "residual is NULL", "bad residual row stride"));
+  DIT_TRY(check_rows(y, y_rs, rows, dim, "y is NULL", "bad y row stride"));
+  DIT_TRY(check_rows(gate, mod_rs, mod_rows, dim, "gate is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(residual, res_rs, rows, dim), rows_span(y, y_rs, rows, dim)};
+  const Span cs[] = {rows_span(gate, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 2, cs, 1));
+  dit::GateAddArgs a{static_cast<uint16_t *>(out), u16(residual), u16(y), u16(gate), out_rs,
+                     res_rs, y_rs, mod_rs, rows, dim, rows / mod_rows};
+  return hip_status(dit::launch_residual_gate_add(a, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Segments of a [batch, tokens, heads*128] view with the given strides.
+Span token_span(const void *p, int64_t ts, int64_t bs, int64_t batch, int64_t tokens,
+                int64_t width) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  if (batch <= 1 || (ts > 0 && bs % ts == 0 && bs >= tokens * ts))
+    return Span{base, ts * 2, (batch <= 1 ? 0 : (batch - 1) * (ts > 0 ? bs / ts : 0)) + tokens,
+                width * 2};
+  return Span{base, 0, 1, ((batch - 1) * bs + (tokens - 1) * ts + width) * 2};
+}
+
+dit_status_t check_stream(const dit_qkv_stream_t *st, int64_t batch, int64_t width) {
+  if (st->tokens < 0) return fail(DIT_ERR_INVALID, "negative token count");
+  if (st->tokens == 0) return DIT_OK;
+  if (!st->q || !st->k || !st->v || !st->q_weight || !st->k_weight)
+    return fail(DIT_ERR_INVALID, "stream pointer is NULL");
+  if (st->tok_stride < 0 || st->batch_stride < 0)
+    return fail(DIT_ERR_INVALID, "negative stream stride");
+  if ((st->tokens > 1 && st->tok_stride < width) || st->tok_stride % 8 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "stream token stride");
+  if (batch > 1 && (st->batch_stride % 8 != 0 || st->batch_stride < width))
+    return fail(DIT_ERR_UNSUPPORTED, "stream batch stride");
+  const void *ps[] = {st->q, st->k, st->v, st->q_weight, st->k_weight};
+  for (const void *p : ps)
+    if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "stream pointer is not 16-byte aligned");
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out,
+                                         int64_t out_tok_stride, int64_t out_batch_stride,
+                                         const dit_qkv_stream_t *txt, const dit_qkv_stream_t *img,
+                                         const float *cos, const float *sin, int64_t batch,
+                                         int64_t heads, int64_t head_dim, float eps, int mode,
+                                         hipStream_t stream) {
+  if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
+    return fail(DIT_ERR_INVALID, "unknown mode");
+  if (batch < 0 || heads < 0 || head_dim < 0) return fail(DIT_ERR_INVALID, "negative size");
+  const dit_qkv_stream_t empty{};
+  const dit_qkv_stream_t *st_txt = txt ? txt : &empty;
+  const dit_qkv_stream_t *st_img = img ? img : &empty;
+  if (st_txt->tokens < 0 || st_img->tokens < 0)
+    return fail(DIT_ERR_INVALID, "negative token count");
+  const int64_t s_total = st_txt->tokens + st_img->tokens;
+  if (batch == 0 || heads == 0 || s_total == 0) return DIT_OK;
+  if (head_dim != DIT_QK_HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "head_dim != 128");
+  if (heads > 64) return fail(DIT_ERR_UNSUPPORTED, "heads > 64");
+  const int64_t width = heads * head_dim;
+  DIT_TRY(check_stream(st_txt, batch, width));
+  DIT_TRY(check_stream(st_img, batch, width));
+  if (!q_out || !k_out || !v_out || !cos || !sin)
+    return fail(DIT_ERR_INVALID, "output or table pointer is NULL");
+  if (out_tok_stride < 0 || out_batch_stride < 0)
+    return fail(DIT_ERR_INVALID, "negative output stride");
+  if ((s_total > 1 && out_tok_stride < width) || out_tok_stride % 8 != 0 ||
+      (batch > 1 && (out_batch_stride % 8 != 0 || out_batch_stride < width)))
+    return fail(DIT_ERR_UNSUPPORTED, "output strides");
+  const void *ps[] = {q_out, k_out, v_out, cos, sin};
+  for (const void *p : ps)
+    if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "pointer is not 16-byte aligned");
+  if ((batch * s_total + 3) / 4 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
+
+  const Span outs[3] = {token_span(q_out, out_tok_stride, out_batch_stride, batch, s_total, width),
+                        token_span(k_out, out_tok_stride, out_batch_stride, batch, s_total, width),
+                        token_span(v_out, out_tok_stride, out_batch_stride, batch, s_total, width)};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (spans_overlap(outs[i], outs[j]))
+        return fail(DIT_ERR_INVALID, "joint outputs overlap each other");
+  Span ins[12];
+  int n = 0;
+  const dit_qkv_stream_t *sts[2] = {st_txt, st_img};
+  for (const dit_qkv_stream_t *st : sts) {
+    if (st->tokens == 0) continue;
+    for (const void *p : {st->q, st->k, st->v})
+      ins[n++] = token_span(p, st->tok_stride, st->batch_stride, batch, st->tokens, width);
+    ins[n++] = Span{reinterpret_cast<uintptr_t>(st->q_weight), 0, 1, head_dim * 2};
+    ins[n++] = Span{reinterpret_cast<uintptr_t>(st->k_weight), 0, 1, head_dim * 2};
+  }
+  ins[n++] = Span{reinterpret_cast<uintptr_t>(cos), 0, 1, s_total * (head_dim / 2) * 4};
+  ins[n++] = Span{reinterpret_cast<uintptr_t>(sin), 0, 1, s_total * (head_dim / 2) * 4};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < n; ++j)
+      if (spans_overlap(outs[i], ins[j])) return fail(DIT_ERR_INVALID, "output overlaps an input");
+
+  dit::QkvArgs a;
+  a.q_out = static_cast<uint16_t *>(q_out);
+  a.k_out = static_cast<uint16_t *>(k_out);
+  a.v_out = static_cast<uint16_t *>(v_out);
+  a.out_ts = out_tok_stride;
+  a.out_bs = out_batch_stride;
+  const dit_qkv_stream_t *src[2] = {st_txt, st_img};
+  dit::QkvStreamArgs *dst[2] = {&a.txt, &a.img};
+  for (int i = 0; i < 2; ++i) {
+    dst[i]->q = u16(src[i]->q);
+    dst[i]->k = u16(src[i]->k);
+    dst[i]->v = u16(src[i]->v);
+    dst[i]->q_weight = u16(src[i]->q_weight);
+    dst[i]->k_weight = u16(src[i]->k_weight);
+    dst[i]->tok_stride = src[i]->tok_stride;
+    dst[i]->batch_stride = src[i]->batch_stride;
+    dst[i]->tokens = src[i]->tokens;
+  }
+  a.cos = cos;
+  a.sin = sin;
+  a.batch = batch;
+  a.heads = heads;
+  a.s_total = s_total;
+  a.eps = eps;
+  return hip_status(dit::launch_qk_norm_rope(a, mode, stream));
+}
+
+// ---------------------------------------------------------------------------
+// Probes
+// ---------------------------------------------------------------------------
+extern "C" {
+
+dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t stream) {
+  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (n == 0) return DIT_OK;
+  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
+  return hip_status(dit::launch_probe_bf16_round(out, in, n, stream));
+}
+
+dit_status_t dit_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
+                             hipStream_t stream) {
+  if (op < DIT_PROBE_ONE_PLUS || op > DIT_PROBE_RMS_RSTD) return fail(DIT_ERR_INVALID, "bad op");
+  if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
+    return fail(DIT_ERR_INVALID, "unknown mode");
+  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (n == 0) return DIT_OK;
+  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
+  return hip_status(dit::launch_probe_unary(op, out, in, n, mode, stream));
+}
+
+dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, int64_t n, int mode,
+                           hipStream_t stream) {
+  if (op < DIT_PROBE_DIV || op > DIT_PROBE_RSQRT) return fail(DIT_ERR_INVALID, "bad op");
+  if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
+    return fail(DIT_ERR_INVALID, "unknown mode");
+  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (n == 0) return DIT_OK;
+  if (!out || !a || (op == DIT_PROBE_DIV && !b)) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
+  return hip_status(dit::launch_probe_f32(op, out, a, b, n, mode, stream));
+}
+
+dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
+                               hipStream_t stream) {
+  if (rows < 0 || dim < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (head != 0 && head != 1) return fail(DIT_ERR_INVALID, "head must be 0 or 1");
+  if (rows == 0) return DIT_OK;
+  if (!out || !t) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (head == 0 && (dim == 0 || dim > DIT_MAX_DIM || dim % 8 != 0))
+    return fail(DIT_ERR_UNSUPPORTED, "dim must be a multiple of 8 in [8, 8192]");
+  if (head == 1 && dim != DIT_QK_HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "dim must be 128");
+  if (rows > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
+  return hip_status(dit::launch_probe_row_sum(out, t, rows, dim, head, stream));
+}
+
+}  // extern "C"

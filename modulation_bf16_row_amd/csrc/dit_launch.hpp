@@ -1,0 +1,72 @@
+// dit_launch.hpp -- internal kernel argument blocks and launchers.  The
+// C-ABI layer validates every argument before it fills these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+struct LnModArgs {
+  uint16_t *out;
+  const uint16_t *x, *scale, *shift;
+  int64_t out_rs, x_rs, mod_rs;
+  int64_t rows, dim, per_mod;  // per_mod = rows / mod_rows
+  float eps;
+};
+
+struct RmsScaleArgs {
+  uint16_t *out;
+  const uint16_t *x, *weight, *scale;
+  int64_t out_rs, x_rs, mod_rs;
+  int64_t rows, dim, per_mod;
+  float eps;
+};
+
+struct RmsTanhArgs {
+  uint16_t *out;
+  const uint16_t *x, *residual, *weight, *gate;
+  int64_t out_rs, x_rs, res_rs, mod_rs;
+  int64_t rows, dim, per_mod;
+  float eps;
+};
+
+struct GateAddArgs {
+  uint16_t *out;
+  const uint16_t *residual, *y, *gate;
+  int64_t out_rs, res_rs, y_rs, mod_rs;
+  int64_t rows, dim, per_mod;
+};
+
+struct QkvStreamArgs {
+  const uint16_t *q, *k, *v;
+  const uint16_t *q_weight, *k_weight;
+  int64_t tok_stride, batch_stride;
+  int64_t tokens;
+};
+
+struct QkvArgs {
+  uint16_t *q_out, *k_out, *v_out;
+  int64_t out_ts, out_bs;
+  QkvStreamArgs txt, img;
+  const float *cos, *sin;
+  int64_t batch, heads, s_total;
+  float eps;
+};
+
+hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s);
+hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s);
+hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStream_t s);
+hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t s);
+hipError_t launch_qk_norm_rope(const QkvArgs &a, int mode, hipStream_t s);
+
+// Device-primitive probes (exhaustive tests of the kernels' own helpers).
+hipError_t launch_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t s);
+hipError_t launch_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
+                              hipStream_t s);
+hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, int64_t n,
+                            int mode, hipStream_t s);
+hipError_t launch_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
+                                hipStream_t s);
+
+}  // namespace dit

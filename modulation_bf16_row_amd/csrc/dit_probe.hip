@@ -1,0 +1,108 @@
+// dit_probe.hip -- kernels that run the epilogue kernels' own device
+// primitives (bf16 rounding, 1 + scale, tanh, the RMSNorm rstd chain, fp32
+// division / square root, the two reduction trees) over caller arrays, so
+// the tests can check each primitive exhaustively against the oracle.
+#include "dit_device.hpp"
+#include "dit_launch.hpp"
+
+namespace dit {
+
+__global__ void k_probe_bf16_round(uint16_t *out, const float *in, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint16_t)(pack(in[i], 0.0f) & 0xFFFFu);
+}
+
+// op 0: bf(1 + s); op 1: tanh to bf16; op 2: bf(1 / sqrt(v)) as in RMSNorm.
+template <int MODE>
+__global__ void k_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = __uint_as_float((uint32_t)in[i] << 16);
+  float r;
+  if (op == 0)
+    r = round1(1.0f + v);
+  else if (op == 1)
+    r = tanh_bf16<MODE>(v);
+  else
+    r = round1(rsqrt_mode<MODE>(v));
+  out[i] = (uint16_t)(__float_as_uint(r) >> 16);
+}
+
+// op 0: a / b; op 1: sqrt(a); op 2: 1 / sqrt(a) (rsqrt_mode).
+template <int MODE>
+__global__ void k_probe_f32(int op, float *out, const float *a, const float *b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float r;
+  if (op == 0)
+    r = a[i] / b[i];
+  else if (op == 1)
+    r = __builtin_sqrtf(a[i]);
+  else
+    r = rsqrt_mode<MODE>(a[i]);
+  out[i] = r;
+}
+
+// head == 0: one wave per row of `dim` terms, R(dim) order.
+// head == 1: 16 lanes per 128-term group (dim must be 128).
+__global__ __launch_bounds__(64) void k_probe_row_sum(float *out, const float *t, int64_t rows,
+                                                      int64_t dim, int head) {
+  const int lane = threadIdx.x;
+  if (head == 0) {
+    const int64_t row = blockIdx.x;
+    if (row >= rows) return;
+    const float *tr = t + row * dim;
+    float p = 0.0f;
+    for (int c = 0; 512 * c < dim; ++c)
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = 512 * c + 8 * lane + j;
+        if (e < dim) p = p + tr[e];
+      }
+    p = wave_sum(p);
+    if (lane == 0) out[row] = p;
+  } else {
+    const int64_t grp = (int64_t)blockIdx.x * 4 + (lane >> 4);
+    if (grp >= rows) return;                     // whole 16-lane groups exit together
+    const float *tr = t + grp * 128 + 8 * (lane & 15);
+    float p = 0.0f;
+    for (int j = 0; j < 8; ++j) p = p + tr[j];
+    p = group16_sum(p);
+    if ((lane & 15) == 0) out[grp] = p;
+  }
+}
+
+static dim3 flat_grid(int64_t n, int block) { return dim3((unsigned)((n + block - 1) / block)); }
+
+hipError_t launch_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_probe_bf16_round, flat_grid(n, 256), dim3(256), 0, s, out, in, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
+                              hipStream_t s) {
+  if (mode == kFast)
+    hipLaunchKernelGGL(k_probe_unary<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, in, n);
+  else
+    hipLaunchKernelGGL(k_probe_unary<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, in,
+                       n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, int64_t n,
+                            int mode, hipStream_t s) {
+  if (mode == kFast)
+    hipLaunchKernelGGL(k_probe_f32<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b, n);
+  else
+    hipLaunchKernelGGL(k_probe_f32<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b,
+                       n);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
+                                hipStream_t s) {
+  const dim3 grid = head ? flat_grid(rows, 4) : dim3((unsigned)rows);
+  hipLaunchKernelGGL(k_probe_row_sum, grid, dim3(64), 0, s, out, t, rows, dim, head);
+  return hipGetLastError();
+}
+
+}  // namespace dit
