@@ -189,6 +189,24 @@ def cpu_baseline(blk, qkv, gpu_out):
                 seconds_per_op={k: round(v, 3) for k, v in t_ops.items()}), exact
 
 
+def copy_ceiling(torch, nbytes=1 << 30, reps=5):
+    """Practical HBM ceiling: torch's device copy of a 1 GiB bf16 buffer (2 GiB
+    moved per copy, far beyond the Infinity Cache), GB/s of read + write."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    sec = s.elapsed_time(e) * 1e-3 / reps
+    del src, dst
+    return round(2 * nbytes / sec / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +271,7 @@ def main():
                     mode=args.mode, step_bytes=step_bytes, host_wall_ms_per_step=round(
                         1000 * wall / args.steps, 4)),
         roofline=roofline, kernels=per_kernel,
+        copy_ceiling_gbs=copy_ceiling(torch),
     )
     if not args.no_cpu:
         gpu_out = {k: sets[0].out[k].cpu().view(torch.int16).numpy().view(np.uint16)

@@ -47,7 +47,9 @@
  *   sums use the order R(D) below.  The output is bit-for-bit deterministic.
  *   DIT_MODE_FAST: hardware reciprocal square root, fused multiply-add inside
  *   the sums and the RoPE products, and a plain binary32 tanh; every bf16
- *   rounding point of the lossless chain is kept.
+ *   rounding point of the lossless chain is kept.  The hardware rsqrt reads a
+ *   subnormal argument as zero (result +inf); the norms only reach that with
+ *   eps < 2^-126.
  * Reduction order R(D) (D <= 8192, D % 8 == 0).  A 64-lane wave holds one
  *   row; lane l owns elements 512c + 8l + j (j = 0..7) of chunk c.  Each lane
  *   adds its own terms to +0 in (c, j) order; then, for m = 1, 2, 4, 8, 16,

@@ -66,6 +66,13 @@ def test_unary_fast_within_one_step(op, name):
     got = m().dit_probe_unary(op, h, "fast").cpu().numpy().view(np.uint16)
     ref = {1: oracle.tanh_bf16, 2: oracle.rms_rstd}[op](ALL16)
     fin = ~is_nan_bits(ref) & ~is_nan_bits(got)
+    if op == 2:
+        # The hardware rsqrt reads subnormal inputs as zero (result +inf).  The
+        # norms never feed it one when eps > 0: v = bf(ms + eps) >= eps.
+        exp = (ALL16 >> 7) & 0xFF
+        sub = (exp == 0) & ((ALL16 & 0x7F) != 0)
+        assert np.all(got[sub & (ALL16 < 0x8000)] == 0x7F80)
+        fin &= ~sub
     assert ulp_distance(got[fin], ref[fin]).max() <= 1
 
 

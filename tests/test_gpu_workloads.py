@@ -1,0 +1,256 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times, plus FAST-mode tolerances and the 50-iteration chain.
+
+- Qwen-Image 1024x1024 block ([9216, 3072], per-batch modulation): all four
+  row ops compared with the oracle on every row.
+- Qwen-Image QKV epilogue (merged QKV [2, 4096|512, 9216] -> joint
+  [2, 4608, 24, 128]): every element compared.
+- Wan 720p block ([75600, 5120], per-token scale/shift/gate, and a per-batch
+  gate): LN + modulate and RMSNorm-tanh-residual on the whole tensor, the
+  oracle on a sample of rows (rows are independent), plus the first and last
+  rows.
+- FAST mode against LOSSLESS: at most 2 bf16 steps, measured in steps of the
+  magnitude entering the last rounding, and >= 99.9% of elements within 1
+  step (literal); the literal maximum is printed.
+- Chain: 50 iterations of LN+modulate -> gate-add -> RMSNorm-scale fed back;
+  LOSSLESS equals the oracle at every iteration on sampled rows; FAST stays
+  >= 40 dB PSNR against LOSSLESS after 50 iterations.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact import ulp_distance, value_of_bf16
+from gpu_util import assert_bits_equal, dev, host, say
+from modulation_bf16_row_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import modulation_bf16_row_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+
+
+def m():
+    import modulation_bf16_row_amd as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def qwen():
+    return synth.qwen_image_block()
+
+
+def test_qwen_block_full_size(qwen):
+    w = qwen
+    x, sc, sh, g, s2, wt, res = (dev(w[k]) for k in ("x", "scale", "shift", "gate", "scale2",
+                                                      "weight", "residual"))
+    say("qwen block ln_modulate [9216,3072]")
+    h = m().dit_ln_modulate(x, sc, sh, w["eps"])
+    assert_bits_equal(host(h), oracle.ln_modulate(w["x"], w["scale"], w["shift"], w["eps"]), "ln")
+    say("qwen block rmsnorm_scale")
+    o = m().dit_rmsnorm_scale(x, wt, s2, w["eps"])
+    assert_bits_equal(host(o), oracle.rmsnorm_scale(w["x"], w["weight"], w["scale2"], w["eps"]),
+                      "rms")
+    say("qwen block rmsnorm_tanh_residual")
+    o = m().dit_rmsnorm_tanh_residual(x, res, wt, g, w["eps"])
+    assert_bits_equal(host(o), oracle.rmsnorm_tanh_residual(w["x"], w["residual"], w["weight"],
+                                                            w["gate"], w["eps"]), "tanh")
+    say("qwen block residual_gate_add")
+    o = m().dit_residual_gate_add(res, h, g)
+    ref_h = host(h)
+    assert_bits_equal(host(o), oracle.residual_gate_add(w["residual"], ref_h, w["gate"]), "gate")
+
+
+def _qkv_views(a, H, Dh=128):
+    if isinstance(a, np.ndarray):
+        return [a[:, :, i * H * Dh:(i + 1) * H * Dh].reshape(a.shape[0], a.shape[1], H, Dh)
+                for i in range(3)]
+    return [a[:, :, i * H * Dh:(i + 1) * H * Dh].view(a.shape[0], a.shape[1], H, Dh)
+            for i in range(3)]
+
+
+def _qkv_run(q, mode):
+    H = q["heads"]
+    tq, tk, tv = _qkv_views(dev(q["txt_qkv"]), H)
+    iq, ik, iv = _qkv_views(dev(q["img_qkv"]), H)
+    return [host(t) for t in m().dit_qk_norm_rope(
+        dict(q=tq, k=tk, v=tv, q_weight=dev(q["txt_q_weight"]), k_weight=dev(q["txt_k_weight"])),
+        dict(q=iq, k=ik, v=iv, q_weight=dev(q["img_q_weight"]), k_weight=dev(q["img_k_weight"])),
+        torch.from_numpy(q["cos"]).cuda(), torch.from_numpy(q["sin"]).cuda(), q["eps"],
+        mode=mode)]
+
+
+@pytest.fixture(scope="module")
+def qkv():
+    return synth.qwen_image_qkv()
+
+
+def test_qwen_qkv_full_size(qkv):
+    q = qkv
+    say("qwen qkv [2,4608,24,128]")
+    got = _qkv_run(q, "lossless")
+    H = q["heads"]
+    tq, tk, tv = _qkv_views(q["txt_qkv"], H)
+    iq, ik, iv = _qkv_views(q["img_qkv"], H)
+    ref = oracle.qk_norm_rope(
+        dict(q=tq, k=tk, v=tv, q_weight=q["txt_q_weight"], k_weight=q["txt_k_weight"]),
+        dict(q=iq, k=ik, v=iv, q_weight=q["img_q_weight"], k_weight=q["img_k_weight"]),
+        q["cos"], q["sin"], q["eps"])
+    for name, g, r in zip("qkv", got, ref):
+        assert_bits_equal(g, r, name)
+
+
+@pytest.fixture(scope="module")
+def wan():
+    return synth.wan_720p_block()
+
+
+def _sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.integers(0, n, k)]))
+
+
+def test_wan_block_full_size_sampled(wan):
+    w = wan
+    rows = w["x"].shape[0]
+    x, sc, sh, g, wt, res = (dev(w[k]) for k in ("x", "scale", "shift", "gate", "weight",
+                                                 "residual"))
+    idx = _sample_rows(rows, 600, 5)
+    say("wan ln_modulate per-token [75600,5120]")
+    out = host(m().dit_ln_modulate(x, sc, sh, w["eps"]))[idx]
+    ref = oracle.ln_modulate(w["x"][idx], w["scale"][idx], w["shift"][idx], w["eps"])
+    assert_bits_equal(out, ref, "wan ln per-token")
+    say("wan rmsnorm_tanh_residual per-token gate")
+    out = host(m().dit_rmsnorm_tanh_residual(x, res, wt, g, w["eps"]))[idx]
+    ref = oracle.rmsnorm_tanh_residual(w["x"][idx], w["residual"][idx], w["weight"],
+                                       w["gate"][idx], w["eps"])
+    assert_bits_equal(out, ref, "wan tanh per-token")
+    say("wan rmsnorm_tanh_residual per-batch gate")
+    g1 = g[:1]
+    out = host(m().dit_rmsnorm_tanh_residual(x, res, wt, g1, w["eps"]))[idx]
+    ref = oracle.rmsnorm_tanh_residual(w["x"][idx], w["residual"][idx], w["weight"],
+                                       w["gate"][:1], w["eps"])
+    assert_bits_equal(out, ref, "wan tanh per-batch")
+
+
+# --------------------------------------------------------------------------------------
+# FAST mode
+# --------------------------------------------------------------------------------------
+
+def _bf16_step(v):
+    """Size of one bf16 step at magnitude |v| (normal range)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def _fast_report(name, fast, lossless, scale_mag=None):
+    d = ulp_distance(fast, lossless)
+    frac1 = float((d <= 1).mean())
+    lit = int(d.max())
+    if scale_mag is None:
+        scaled = float(d.max())
+    else:
+        err = np.abs(value_of_bf16(fast) - value_of_bf16(lossless))
+        scaled = float((err / _bf16_step(scale_mag)).max())
+    say(f"FAST {name}: literal max {lit} steps, <=1 step {100 * frac1:.4f}%, "
+        f"max in steps of the last rounding's input {scaled:.3f}")
+    return lit, frac1, scaled
+
+
+def test_fast_mode_tolerances(qwen, qkv):
+    w = qwen
+    x, sc, sh, g, s2, wt, res = (dev(w[k]) for k in ("x", "scale", "shift", "gate", "scale2",
+                                                      "weight", "residual"))
+    M = m()
+    say("FAST vs LOSSLESS, qwen block")
+    ln_l = host(M.dit_ln_modulate(x, sc, sh, w["eps"], "lossless"))
+    ln_f = host(M.dit_ln_modulate(x, sc, sh, w["eps"], "fast"))
+    # magnitude entering the last rounding: max(|p|, |shift|), p = bf(n * bf(1 + scale))
+    per = ln_l.shape[0] // w["scale"].shape[0]
+    rows = _sample_rows(ln_l.shape[0], 400, 9)
+    mag = np.empty((len(rows), ln_l.shape[1]))
+    for i, r in enumerate(rows):
+        n, _ = oracle.ln_row(w["x"][r], w["eps"])
+        s1 = value_of_bf16(oracle.one_plus(w["scale"][r // per]))
+        p = value_of_bf16(oracle.bf16_round(value_of_bf16(n) * s1))
+        mag[i] = np.maximum(np.abs(p), np.abs(value_of_bf16(w["shift"][r // per])))
+    _, frac1, _ = _fast_report("ln_modulate (all rows)", ln_f, ln_l)
+    assert frac1 >= 0.999
+    _, _, scaled = _fast_report("ln_modulate (sampled rows, scaled)", ln_f[rows], ln_l[rows], mag)
+    assert scaled <= 2.0
+    for name, fl, ff in (
+            ("rmsnorm_scale", M.dit_rmsnorm_scale(x, wt, s2, w["eps"], "lossless"),
+             M.dit_rmsnorm_scale(x, wt, s2, w["eps"], "fast")),
+            ("rmsnorm_tanh_residual", M.dit_rmsnorm_tanh_residual(x, res, wt, g, w["eps"],
+                                                                  "lossless"),
+             M.dit_rmsnorm_tanh_residual(x, res, wt, g, w["eps"], "fast"))):
+        lit, frac1, _ = _fast_report(name, host(ff), host(fl))
+        assert frac1 >= 0.999
+        assert lit <= 2 or name == "rmsnorm_tanh_residual"
+    gl = host(M.dit_residual_gate_add(res, x, g, "lossless"))
+    gf = host(M.dit_residual_gate_add(res, x, g, "fast"))
+    assert np.array_equal(gl, gf)                  # identical arithmetic in both modes
+    say("FAST vs LOSSLESS, qwen qkv")
+    ql = _qkv_run(qkv, "lossless")
+    qf = _qkv_run(qkv, "fast")
+    for name, a, b in zip("qk", qf[:2], ql[:2]):
+        lit, frac1, _ = _fast_report("qk_norm_rope " + name, a, b)
+        assert frac1 >= 0.999
+    assert np.array_equal(qf[2], ql[2])
+
+
+# --------------------------------------------------------------------------------------
+# 50-iteration chain
+# --------------------------------------------------------------------------------------
+
+def _chain_gpu(w, mode, iters, keep_rows):
+    M = m()
+    x = dev(w["x"])
+    sc, sh, g, s2, wt = (dev(w[k]) for k in ("scale", "shift", "gate", "scale2", "weight"))
+    h = torch.empty_like(x)
+    r = torch.empty_like(x)
+    trace = []
+    for _ in range(iters):
+        M.dit_ln_modulate(x, sc, sh, w["eps"], mode, out=h)
+        M.dit_residual_gate_add(x, h, g, mode, out=r)
+        M.dit_rmsnorm_scale(r, wt, s2, w["eps"], mode, out=x)
+        trace.append(host(x[torch.from_numpy(keep_rows).cuda()]))
+    return host(x), trace
+
+
+def _psnr(ref_bits, got_bits):
+    ref = value_of_bf16(ref_bits)
+    got = value_of_bf16(got_bits)
+    mse = np.mean((ref - got) ** 2)
+    rng = ref.max() - ref.min()
+    return float("inf") if mse == 0 else float(10 * np.log10(rng * rng / mse))
+
+
+def test_chain_50_iterations():
+    w = synth.chain_block()
+    rows = w["x"].shape[0]
+    keep = _sample_rows(rows, 120, 11)
+    say("chain LOSSLESS x50")
+    final_l, trace_l = _chain_gpu(w, "lossless", 50, keep)
+    # oracle on the kept rows (each row's chain only involves that row)
+    per = rows // w["scale"].shape[0]
+    xs = w["x"][keep].copy()
+    mods = keep // per
+    sc, sh, g, s2 = (w[k][mods] for k in ("scale", "shift", "gate", "scale2"))
+    for it in range(50):
+        h = oracle.ln_modulate(xs, sc, sh, w["eps"])
+        r = oracle.residual_gate_add(xs, h, g)
+        xs = oracle.rmsnorm_scale(r, w["weight"], s2, w["eps"])
+        assert_bits_equal(trace_l[it], xs, f"chain iteration {it + 1}")
+    say("chain FAST x50")
+    final_f, trace_f = _chain_gpu(w, "fast", 50, keep)
+    psnr = _psnr(final_l, final_f)
+    curve = [round(_psnr(a, b), 2) for a, b in zip(trace_l[::10], trace_f[::10])]
+    say(f"chain PSNR FAST vs LOSSLESS after 50 iterations: {psnr:.2f} dB; sampled-row "
+        f"curve every 10 iterations: {curve}")
+    assert psnr >= 40.0
