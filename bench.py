@@ -123,26 +123,22 @@ class BufferSet:
 
 
 def run_step(m, s, mode, ev=None):
-    """Launches the five epilogues; ev[k] = (start, end) events per kernel."""
-    def rec(k, i):
+    """Launches the five epilogues.  With ev, ev[k] = (start, stop) HIP events
+    that the dispatch of kernel k records itself (dit_time_next_launch)."""
+    def timed(k):
         if ev is not None:
-            ev[k][i].record()
-    rec("ln_modulate", 0)
+            m.dit_time_next_launch(ev[k][0], ev[k][1])
+    timed("ln_modulate")
     m.dit_ln_modulate(s.x, s.scale, s.shift, EPS, mode, out=s.out["ln_modulate"])
-    rec("ln_modulate", 1)
-    rec("rmsnorm_scale", 0)
+    timed("rmsnorm_scale")
     m.dit_rmsnorm_scale(s.x, s.w, s.scale2, EPS, mode, out=s.out["rmsnorm_scale"])
-    rec("rmsnorm_scale", 1)
-    rec("rmsnorm_tanh_residual", 0)
+    timed("rmsnorm_tanh_residual")
     m.dit_rmsnorm_tanh_residual(s.x, s.res, s.w, s.gate, EPS, mode,
                                 out=s.out["rmsnorm_tanh_residual"])
-    rec("rmsnorm_tanh_residual", 1)
-    rec("residual_gate_add", 0)
+    timed("residual_gate_add")
     m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.out["residual_gate_add"])
-    rec("residual_gate_add", 1)
-    rec("qk_norm_rope", 0)
+    timed("qk_norm_rope")
     m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode, out=s.qkv_out)
-    rec("qk_norm_rope", 1)
 
 
 def cpu_baseline(blk, qkv, gpu_out):
@@ -235,6 +231,10 @@ def main():
 
     ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
               for _ in range(args.steps)] for k in KERNELS}
+    for k in KERNELS:                  # record once so the HIP events exist
+        for pair in ev[k]:
+            for e in pair:
+                e.record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()

@@ -67,6 +67,7 @@ SIGNATURES = {
     "dit_probe_unary": [_int, _vp, _vp, _i64, _int, _vp],
     "dit_probe_f32": [_int, _vp, _vp, _vp, _i64, _int, _vp],
     "dit_probe_row_sum": [_vp, _vp, _i64, _i64, _int, _vp],
+    "dit_time_next_launch": [_vp, _vp],
 }
 
 
@@ -284,6 +285,13 @@ def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None):
                                   cos.data_ptr(), sin.data_ptr(), B, H, Dh, eps, _mode(mode),
                                   _stream(ref)))
     return out
+
+
+def dit_time_next_launch(start, stop):
+    """Makes the next epilogue call on this thread record `start` / `stop`
+    (torch.cuda.Event objects that have been recorded once, so that they
+    exist) around its kernel, from within the dispatch."""
+    _check(lib().dit_time_next_launch(_vp(start.cuda_event), _vp(stop.cuda_event)))
 
 
 # --- probes of the device primitives ---------------------------------------------------

@@ -40,12 +40,13 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, build_dir, extra):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", *COMMON, *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [_hipcc(), *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        cmd = [_hipcc(), *COMMON, *extra, "-D__HIP_PLATFORM_AMD__", "-c",
+               os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,17 +59,21 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 4, lib: str = LIB, extra_flags=()) -> str:
+    """Compiles and links the library; `lib` and `extra_flags` allow side
+    builds (e.g. with -D macros) without touching the default one."""
+    build_dir = BUILD if lib == LIB else os.path.join(BUILD, os.path.basename(lib) + ".d")
+    os.makedirs(build_dir, exist_ok=True)
+    extra = list(extra_flags)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -16,10 +16,13 @@
 #include "dit.h"
 #include "dit_launch.hpp"
 #include "dit_probe.h"
+#include "dit_timing.h"
 
 namespace {
 
 thread_local const char *g_reason = "";
+thread_local hipEvent_t g_time_start = nullptr;
+thread_local hipEvent_t g_time_stop = nullptr;
 
 dit_status_t fail(dit_status_t s, const char *why) {
   g_reason = why;
@@ -125,9 +128,23 @@ const uint16_t *u16(const void *p) { return static_cast<const uint16_t *>(p); }
 
 }  // namespace
 
+bool dit::take_timing_events(hipEvent_t *start, hipEvent_t *stop) {
+  if (!g_time_start && !g_time_stop) return false;
+  *start = g_time_start;
+  *stop = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
+  return true;
+}
+
 extern "C" {
 
 int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+dit_status_t dit_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+  g_time_start = start;
+  g_time_stop = stop;
+  return DIT_OK;
+}
 
 const char *dit_status_string(dit_status_t s) {
   switch (s) {

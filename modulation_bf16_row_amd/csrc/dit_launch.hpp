@@ -2,10 +2,27 @@
 // C-ABI layer validates every argument before it fills these.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dit {
+
+// Event pair registered by dit_time_next_launch() on the calling thread;
+// returns false when none is pending.  Taking the pair clears it.
+bool take_timing_events(hipEvent_t *start, hipEvent_t *stop);
+
+// Kernel launch that, when a timing pair is pending, lets the dispatch
+// itself record the start and stop events (hipExtLaunchKernelGGL).
+#define DIT_LAUNCH(kernel, grid, block, shmem, stream, ...)                              \
+  do {                                                                                   \
+    hipEvent_t dit_ev_start_, dit_ev_stop_;                                              \
+    if (::dit::take_timing_events(&dit_ev_start_, &dit_ev_stop_))                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, dit_ev_start_, dit_ev_stop_, \
+                            0, __VA_ARGS__);                                             \
+    else                                                                                 \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);               \
+  } while (0)
 
 struct LnModArgs {
   uint16_t *out;
@@ -13,6 +30,7 @@ struct LnModArgs {
   int64_t out_rs, x_rs, mod_rs;
   int64_t rows, dim, per_mod;  // per_mod = rows / mod_rows
   float eps;
+  int64_t rows_per_wave;       // set by the launcher
 };
 
 struct RmsScaleArgs {
@@ -21,6 +39,7 @@ struct RmsScaleArgs {
   int64_t out_rs, x_rs, mod_rs;
   int64_t rows, dim, per_mod;
   float eps;
+  int64_t rows_per_wave;
 };
 
 struct RmsTanhArgs {
@@ -29,6 +48,7 @@ struct RmsTanhArgs {
   int64_t out_rs, x_rs, res_rs, mod_rs;
   int64_t rows, dim, per_mod;
   float eps;
+  int64_t rows_per_wave;
 };
 
 struct GateAddArgs {
@@ -36,6 +56,7 @@ struct GateAddArgs {
   const uint16_t *residual, *y, *gate;
   int64_t out_rs, res_rs, y_rs, mod_rs;
   int64_t rows, dim, per_mod;
+  int64_t rows_per_wave;
 };
 
 struct QkvStreamArgs {
@@ -52,6 +73,7 @@ struct QkvArgs {
   const float *cos, *sin;
   int64_t batch, heads, s_total;
   float eps;
+  int64_t tokens_per_wave;     // set by the launcher
 };
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s);

@@ -74,16 +74,16 @@ __global__ __launch_bounds__(64) void k_probe_row_sum(float *out, const float *t
 static dim3 flat_grid(int64_t n, int block) { return dim3((unsigned)((n + block - 1) / block)); }
 
 hipError_t launch_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_probe_bf16_round, flat_grid(n, 256), dim3(256), 0, s, out, in, n);
+  DIT_LAUNCH(k_probe_bf16_round, flat_grid(n, 256), dim3(256), 0, s, out, in, n);
   return hipGetLastError();
 }
 
 hipError_t launch_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
                               hipStream_t s) {
   if (mode == kFast)
-    hipLaunchKernelGGL(k_probe_unary<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, in, n);
+    DIT_LAUNCH(k_probe_unary<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, in, n);
   else
-    hipLaunchKernelGGL(k_probe_unary<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, in,
+    DIT_LAUNCH(k_probe_unary<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, in,
                        n);
   return hipGetLastError();
 }
@@ -91,9 +91,9 @@ hipError_t launch_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t
 hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, int64_t n,
                             int mode, hipStream_t s) {
   if (mode == kFast)
-    hipLaunchKernelGGL(k_probe_f32<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b, n);
+    DIT_LAUNCH(k_probe_f32<kFast>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b, n);
   else
-    hipLaunchKernelGGL(k_probe_f32<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b,
+    DIT_LAUNCH(k_probe_f32<kLossless>, flat_grid(n, 256), dim3(256), 0, s, op, out, a, b,
                        n);
   return hipGetLastError();
 }
@@ -101,7 +101,7 @@ hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, 
 hipError_t launch_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
                                 hipStream_t s) {
   const dim3 grid = head ? flat_grid(rows, 4) : dim3((unsigned)rows);
-  hipLaunchKernelGGL(k_probe_row_sum, grid, dim3(64), 0, s, out, t, rows, dim, head);
+  DIT_LAUNCH(k_probe_row_sum, grid, dim3(64), 0, s, out, t, rows, dim, head);
   return hipGetLastError();
 }
 

@@ -1,38 +1,46 @@
 // dit_rows.hip -- gfx950 kernels for the four row epilogues.
 //
-// Geometry: one 64-lane wave per row, four waves (rows) per 256-thread
-// workgroup.  Lane l owns the 8-element vectors at 512c + 8l of chunk c
-// (c < NC = ceil(dim / 512)), loaded with one 128-bit access each, so a
-// wave-wide load is 1 KiB contiguous.  The row stays in VGPRs between the
-// two LayerNorm passes (at most 16 vectors = 64 VGPRs for dim 8192), so x
-// is read from HBM exactly once.  Row sums follow R(dim): each lane adds
-// its own terms in (chunk, element) order, then a fixed xor butterfly.
+// Geometry.  One 64-lane wave per row at a time; lane l owns the 8-element
+// vectors at 512c + 8l of chunk c (c < NC = ceil(dim / 512)), each moved
+// with one 128-bit access, so a wave-wide access is 1 KiB contiguous.  A
+// wave walks a contiguous run of `rows_per_wave` rows; a 256-thread
+// workgroup (four waves) covers 4 * rows_per_wave consecutive rows.  The
+// row stays in VGPRs between the LayerNorm passes, so x is read from HBM
+// once; latency is hidden by the other waves resident on the SIMD.
+//
+// Modulation operands.  With per-batch modulation (a workgroup's rows meet
+// at most two modulation rows), the workgroup computes the per-element
+// operands once into LDS -- bf(1 + scale) and shift, the RMSNorm weight and
+// scale, tanh(gate), or gate -- and every wave reads them with one 128-bit
+// LDS access per vector.  With per-token modulation each row's operands are
+// loaded (and transformed) by the wave that uses them.
+//
+// Sums follow R(dim): each lane adds its own terms in (chunk, element)
+// order, then a fixed xor butterfly across the 64 lanes.
 //
 // Sources: AdaLN rounding points -- page "基于Agent的SGLang扩散模型Kernel优化实践"
 // (tahou.com), section "数学等价不代表结果完全一致"; native bf16 RMSNorm chain --
 // page "#34085 [diffusion] Clean up kernels and shared fast paths", section
 // "关键源码片段"; rmsnorm+tanh(gate)*x+residual and residual+gate*update --
 // page "AI Agent 驱动的 SGLang Kernel 一等公民", section 0x3 / 3.2.
+#include <stdlib.h>
+
 #include "dit_device.hpp"
 #include "dit_launch.hpp"
 
 namespace dit {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = 64 * kWavesPerBlock;
 
-struct RowCtx {
-  int lane;
-  int64_t row;
-};
-
-__device__ __forceinline__ RowCtx row_ctx() {
-  RowCtx c;
-  c.lane = threadIdx.x & 63;
-  c.row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  return c;
+// Register budget: at least W6 waves per SIMD at dim <= 3072 (NC <= 6),
+// scaled down in proportion for longer rows.
+constexpr int waves_per_simd(int nc, int w6) {
+  return nc <= 6 ? w6 : (w6 * 6 / nc > 1 ? w6 * 6 / nc : 1);
 }
+#define DIT_OCCUPANCY(NC, W6) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NC, W6), 8)))
 
-// Is chunk c of this lane inside the row?  Chunks before the last are full.
+// Chunk c of this lane lies inside the row?  Chunks before the last are full.
 template <int NC>
 __device__ __forceinline__ bool valid(int c, int lane, int dim) {
   return c < NC - 1 || 512 * c + 8 * lane < dim;
@@ -49,69 +57,151 @@ __device__ __forceinline__ void load_row(V8 (&v)[NC], const uint16_t *base, int 
   }
 }
 
-// ---------------------------------------------------------------------------
-// LayerNorm + AdaLN modulate
-// ---------------------------------------------------------------------------
-template <int NC, int MODE>
-__global__ __launch_bounds__(256) void k_ln_modulate(LnModArgs a) {
-  const RowCtx ctx = row_ctx();
-  if (ctx.row >= a.rows) return;
-  const int lane = ctx.lane, dim = (int)a.dim;
-  const int64_t m = ctx.row / a.per_mod;
-
-  V8 xv[NC], sc[NC], sh[NC];
-  load_row<NC>(xv, a.x + ctx.row * a.x_rs, lane, dim);
-  load_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim);
-  load_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim);
-
-  // pass 1: mean
-  float p = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (valid<NC>(c, lane, dim))
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p = p + elem(xv[c], j);
-  const float mean = wave_sum(p) / (float)dim;
-
-  // pass 2: variance of the deviations (recomputed identically below)
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (valid<NC>(c, lane, dim))
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = elem(xv[c], j) - mean;
-        if (MODE == kLossless)
-          q = q + d * d;
-        else
-          q = fmaf(d, d, q);
-      }
-  const float var = wave_sum(q) / (float)dim;
-  const float rho = rsqrt_mode<MODE>(var + a.eps);
-
-  uint16_t *orow = a.out + ctx.row * a.out_rs;
+// One LDS "row" holds NC * 64 vectors of 8 bf16 (vector index = element / 8).
+template <int NC>
+__device__ __forceinline__ void lds_row(V8 (&v)[NC], const uint4 *row, int lane, int dim) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (!valid<NC>(c, lane, dim)) continue;
-    V8 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float n0 = (lo(xv[c].w[k]) - mean) * rho;
-      float n1 = (hi(xv[c].w[k]) - mean) * rho;
-      round2(n0, n1);                                   // LayerNorm output
-      float s0 = 1.0f + lo(sc[c].w[k]);
-      float s1 = 1.0f + hi(sc[c].w[k]);
-      round2(s0, s1);                                   // 1 + scale
-      float p0 = n0 * s0, p1 = n1 * s1;
-      round2(p0, p1);                                   // product
-      o.w[k] = pack(p0 + lo(sh[c].w[k]), p1 + hi(sh[c].w[k]));  // + shift
+    if (valid<NC>(c, lane, dim)) {
+      const uint4 u = row[64 * c + lane];
+      v[c] = V8{{u.x, u.y, u.z, u.w}};
+    } else {
+      v[c] = V8{{0u, 0u, 0u, 0u}};
     }
-    store8(orow + 512 * c + 8 * lane, o);
+  }
+}
+
+__device__ __forceinline__ void lds_put(uint4 *row, int v, const V8 &x) {
+  row[v] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+}
+
+// Rows of this workgroup and of this wave.
+struct Span {
+  int64_t wg_first, wg_last;    // inclusive range of the workgroup (may be empty)
+  int64_t begin, end;           // the wave's run [begin, end)
+};
+
+__device__ __forceinline__ Span spans(int64_t rows, int64_t rpw) {
+  Span s;
+  s.wg_first = (int64_t)blockIdx.x * kWavesPerBlock * rpw;
+  const int64_t wg_end = s.wg_first + kWavesPerBlock * rpw;
+  s.wg_last = (wg_end < rows ? wg_end : rows) - 1;
+  s.begin = s.wg_first + (int64_t)(threadIdx.x >> 6) * rpw;
+  s.end = s.begin + rpw < rows ? s.begin + rpw : rows;
+  return s;
+}
+
+// Modulation rows of the workgroup: m0 = first, count = 1 or 2.
+struct ModSlots {
+  int64_t m0;
+  int count;
+};
+
+__device__ __forceinline__ ModSlots mod_slots(const Span &s, int64_t per_mod) {
+  ModSlots ms;
+  ms.m0 = s.wg_first / per_mod;
+  ms.count = (int)(s.wg_last / per_mod - ms.m0) + 1;
+  return ms;
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm + AdaLN modulate
+// LDS (staged): [slot][0] = bf(1 + scale), [slot][1] = shift.
+// ---------------------------------------------------------------------------
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 4) void k_ln_modulate(LnModArgs a) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  const Span sp = spans(a.rows, a.rows_per_wave);
+  constexpr int kRow = NC * 64;
+  ModSlots ms{0, 0};
+  if (STAGED) {
+    if (sp.wg_first > sp.wg_last) return;                  // whole workgroup idle
+    ms = mod_slots(sp, a.per_mod);
+    const int nv = dim / 8;
+    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
+      const int slot = i / nv, v = i - slot * nv;
+      const int64_t m = ms.m0 + slot;
+      V8 s = load8(a.scale + m * a.mod_rs + 8 * v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s.w[k] = pack(1.0f + lo(s.w[k]), 1.0f + hi(s.w[k]));
+      lds_put(lds + (2 * slot + 0) * kRow, v, s);
+      lds_put(lds + (2 * slot + 1) * kRow, v, load8(a.shift + m * a.mod_rs + 8 * v));
+    }
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 xv[NC];
+    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
+    const int64_t m = r / a.per_mod;
+    V8 s1[NC], sh[NC];
+    if (!STAGED) {
+      load_row<NC>(s1, a.scale + m * a.mod_rs, lane, dim);
+      load_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim);
+    }
+
+    // pass 1: mean
+    float d[NC][8];
+    float p = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (valid<NC>(c, lane, dim))
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          d[c][j] = elem(xv[c], j);
+          p = p + d[c][j];
+        }
+    const float mean = wave_sum(p) / (float)dim;
+
+    // pass 2: deviations and their squares
+    float q = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (valid<NC>(c, lane, dim))
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          d[c][j] = d[c][j] - mean;
+          if (MODE == kLossless)
+            q = q + d[c][j] * d[c][j];
+          else
+            q = fmaf(d[c][j], d[c][j], q);
+        }
+    const float var = wave_sum(q) / (float)dim;
+    const float rho = rsqrt_mode<MODE>(var + a.eps);
+
+    if (STAGED) {
+      const int slot = (int)(m - ms.m0);
+      lds_row<NC>(s1, lds + (2 * slot + 0) * kRow, lane, dim);
+      lds_row<NC>(sh, lds + (2 * slot + 1) * kRow, lane, dim);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          s1[c].w[k] = pack(1.0f + lo(s1[c].w[k]), 1.0f + hi(s1[c].w[k]));  // 1 + scale
+    }
+
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float n0 = d[c][2 * k] * rho, n1 = d[c][2 * k + 1] * rho;
+        round2(n0, n1);                                           // LayerNorm output
+        float p0 = n0 * lo(s1[c].w[k]), p1 = n1 * hi(s1[c].w[k]);
+        round2(p0, p1);                                           // product
+        o.w[k] = pack(p0 + lo(sh[c].w[k]), p1 + hi(sh[c].w[k]));  // + shift
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Native-bf16 RMSNorm: y2 = bf(bf(x * rstd) * w), rstd from the bf16 chain.
+// Native-bf16 RMSNorm: the chain's bf16 rstd of one row.
 // ---------------------------------------------------------------------------
 template <int NC, int MODE>
 __device__ __forceinline__ float rms_rstd(const V8 (&xv)[NC], int lane, int dim, float eps) {
@@ -124,15 +214,16 @@ __device__ __forceinline__ float rms_rstd(const V8 (&xv)[NC], int lane, int dim,
         float t0 = lo(xv[c].w[k]), t1 = hi(xv[c].w[k]);
         t0 = t0 * t0;
         t1 = t1 * t1;
-        round2(t0, t1);                                 // bf16 squares
+        round2(t0, t1);                                  // bf16 squares
         p = p + t0;
         p = p + t1;
       }
-  const float ms = round1(wave_sum(p) / (float)dim);    // bf16 mean square
-  const float v = round1(ms + eps);                     // bf16 (ms + eps)
-  return round1(rsqrt_mode<MODE>(v));                   // bf16 rstd
+  const float ms = round1(wave_sum(p) / (float)dim);     // bf16 mean square
+  const float v = round1(ms + eps);                      // bf16 (ms + eps)
+  return round1(rsqrt_mode<MODE>(v));                    // bf16 rstd
 }
 
+// y2 = bf(bf(x * rstd) * w) for the pair in word xw.
 __device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, uint32_t ww,
                                        float rstd) {
   y0 = lo(xw) * rstd;
@@ -143,159 +234,297 @@ __device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, uint32
   round2(y0, y1);
 }
 
-template <int NC, int MODE>
-__global__ __launch_bounds__(256) void k_rmsnorm_scale(RmsScaleArgs a) {
-  const RowCtx ctx = row_ctx();
-  if (ctx.row >= a.rows) return;
-  const int lane = ctx.lane, dim = (int)a.dim;
-  const int64_t m = ctx.row / a.per_mod;
-
-  V8 xv[NC], wv[NC], sc[NC];
-  load_row<NC>(xv, a.x + ctx.row * a.x_rs, lane, dim);
-  load_row<NC>(wv, a.weight, lane, dim);
-  load_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim);
-
-  const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-
-  uint16_t *orow = a.out + ctx.row * a.out_rs;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (!valid<NC>(c, lane, dim)) continue;
-    V8 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float y0, y1;
-      rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
-      o.w[k] = pack(y0 * lo(sc[c].w[k]), y1 * hi(sc[c].w[k]));
+// LDS (staged): [0] = weight, [1 + slot] = scale.
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale(RmsScaleArgs a) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  const Span sp = spans(a.rows, a.rows_per_wave);
+  constexpr int kRow = NC * 64;
+  ModSlots ms{0, 0};
+  if (STAGED) {
+    if (sp.wg_first > sp.wg_last) return;
+    ms = mod_slots(sp, a.per_mod);
+    const int nv = dim / 8;
+    for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
+      const int t = i / nv, v = i - t * nv;
+      const uint16_t *src = t == 0 ? a.weight : a.scale + (ms.m0 + t - 1) * a.mod_rs;
+      lds_put(lds + t * kRow, v, load8(src + 8 * v));
     }
-    store8(orow + 512 * c + 8 * lane, o);
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 xv[NC], wv[NC], sc[NC];
+    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
+    const int64_t m = r / a.per_mod;
+    if (!STAGED) {
+      load_row<NC>(wv, a.weight, lane, dim);
+      load_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim);
+    }
+    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+    if (STAGED) {
+      lds_row<NC>(wv, lds, lane, dim);
+      lds_row<NC>(sc, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
+    }
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float y0, y1;
+        rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
+        o.w[k] = pack(y0 * lo(sc[c].w[k]), y1 * hi(sc[c].w[k]));
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
   }
 }
 
-template <int NC, int MODE>
-__global__ __launch_bounds__(256) void k_rmsnorm_tanh_residual(RmsTanhArgs a) {
-  const RowCtx ctx = row_ctx();
-  if (ctx.row >= a.rows) return;
-  const int lane = ctx.lane, dim = (int)a.dim;
-  const int64_t m = ctx.row / a.per_mod;
-
-  V8 xv[NC], wv[NC], gv[NC], rv[NC];
-  load_row<NC>(xv, a.x + ctx.row * a.x_rs, lane, dim);
-  load_row<NC>(rv, a.residual + ctx.row * a.res_rs, lane, dim);
-  load_row<NC>(wv, a.weight, lane, dim);
-  load_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim);
-
-  const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-
-  uint16_t *orow = a.out + ctx.row * a.out_rs;
+// LDS (staged): [0] = weight, [1 + slot] = tanh(gate).
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_rmsnorm_tanh_residual(
+    RmsTanhArgs a) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  const Span sp = spans(a.rows, a.rows_per_wave);
+  constexpr int kRow = NC * 64;
+  ModSlots ms{0, 0};
+  if (STAGED) {
+    if (sp.wg_first > sp.wg_last) return;
+    ms = mod_slots(sp, a.per_mod);
+    const int nv = dim / 8;
+    for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
+      const int t = i / nv, v = i - t * nv;
+      if (t == 0) {
+        lds_put(lds, v, load8(a.weight + 8 * v));
+      } else {
+        V8 g = load8(a.gate + (ms.m0 + t - 1) * a.mod_rs + 8 * v);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (!valid<NC>(c, lane, dim)) continue;
-    V8 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float y0, y1;
-      rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
-      float q0 = tanh_bf16<MODE>(lo(gv[c].w[k])) * y0;
-      float q1 = tanh_bf16<MODE>(hi(gv[c].w[k])) * y1;
-      round2(q0, q1);
-      o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
+        for (int k = 0; k < 4; ++k)
+          g.w[k] = pack(tanh_bf16<MODE>(lo(g.w[k])), tanh_bf16<MODE>(hi(g.w[k])));
+        lds_put(lds + t * kRow, v, g);
+      }
     }
-    store8(orow + 512 * c + 8 * lane, o);
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 xv[NC], rv[NC], wv[NC], tau[NC];
+    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC>(rv, a.residual + r * a.res_rs, lane, dim);
+    const int64_t m = r / a.per_mod;
+    if (!STAGED) {
+      load_row<NC>(wv, a.weight, lane, dim);
+      load_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim);
+    }
+    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+    if (STAGED) {
+      lds_row<NC>(wv, lds, lane, dim);
+      lds_row<NC>(tau, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
+    }
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float y0, y1;
+        rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
+        float t0, t1;
+        if (STAGED) {
+          t0 = lo(tau[c].w[k]);
+          t1 = hi(tau[c].w[k]);
+        } else {
+          t0 = tanh_bf16<MODE>(lo(tau[c].w[k]));
+          t1 = tanh_bf16<MODE>(hi(tau[c].w[k]));
+        }
+        float q0 = t0 * y0, q1 = t1 * y1;
+        round2(q0, q1);                                   // bf(tanh(gate) * y2)
+        o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Residual gate-add: out = bf(residual + bf(gate * y)).
+// LDS (staged): [slot] = gate.
 // ---------------------------------------------------------------------------
-template <int NC>
-__global__ __launch_bounds__(256) void k_residual_gate_add(GateAddArgs a) {
-  const RowCtx ctx = row_ctx();
-  if (ctx.row >= a.rows) return;
-  const int lane = ctx.lane, dim = (int)a.dim;
-  const int64_t m = ctx.row / a.per_mod;
-
-  V8 rv[NC], yv[NC], gv[NC];
-  load_row<NC>(rv, a.residual + ctx.row * a.res_rs, lane, dim);
-  load_row<NC>(yv, a.y + ctx.row * a.y_rs, lane, dim);
-  load_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim);
-
-  uint16_t *orow = a.out + ctx.row * a.out_rs;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (!valid<NC>(c, lane, dim)) continue;
-    V8 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float g0 = lo(gv[c].w[k]) * lo(yv[c].w[k]);
-      float g1 = hi(gv[c].w[k]) * hi(yv[c].w[k]);
-      round2(g0, g1);
-      o.w[k] = pack(lo(rv[c].w[k]) + g0, hi(rv[c].w[k]) + g1);
+template <int NC, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 5) void k_residual_gate_add(
+    GateAddArgs a) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  const Span sp = spans(a.rows, a.rows_per_wave);
+  constexpr int kRow = NC * 64;
+  ModSlots ms{0, 0};
+  if (STAGED) {
+    if (sp.wg_first > sp.wg_last) return;
+    ms = mod_slots(sp, a.per_mod);
+    const int nv = dim / 8;
+    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
+      const int t = i / nv, v = i - t * nv;
+      lds_put(lds + t * kRow, v, load8(a.gate + (ms.m0 + t) * a.mod_rs + 8 * v));
     }
-    store8(orow + 512 * c + 8 * lane, o);
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 rv[NC], yv[NC], gv[NC];
+    load_row<NC>(rv, a.residual + r * a.res_rs, lane, dim);
+    load_row<NC>(yv, a.y + r * a.y_rs, lane, dim);
+    const int64_t m = r / a.per_mod;
+    if (STAGED)
+      lds_row<NC>(gv, lds + (int)(m - ms.m0) * kRow, lane, dim);
+    else
+      load_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim);
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float g0 = lo(gv[c].w[k]) * lo(yv[c].w[k]);
+        float g1 = hi(gv[c].w[k]) * hi(yv[c].w[k]);
+        round2(g0, g1);
+        o.w[k] = pack(lo(rv[c].w[k]) + g0, hi(rv[c].w[k]) + g1);
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Launchers: NC = ceil(dim / 512) selects the instantiation.
+// Launch shape.
+//   Staged (per-batch) modulation: a run of rows per wave, aiming at about
+//   kTargetWaves waves in flight (MI355X: 256 CUs x 4 SIMDs x 4), and only
+//   when every workgroup's 4 * rows_per_wave rows meet at most two
+//   modulation rows.
+//   Otherwise (per-token modulation): one row per wave.
 // ---------------------------------------------------------------------------
-static dim3 row_grid(int64_t rows) {
-  return dim3((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+constexpr int64_t kTargetWaves = 4096;
+
+struct Shape {
+  int64_t rows_per_wave;
+  bool staged;
+  dim3 grid;
+};
+
+static Shape row_shape(int64_t rows, int64_t per_mod) {
+  Shape s;
+  s.rows_per_wave = (rows + kTargetWaves - 1) / kTargetWaves;
+#ifdef DIT_TUNING
+  if (const char *e = getenv("DIT_ROWS_PER_WAVE")) s.rows_per_wave = atoll(e);
+#endif
+  if (s.rows_per_wave < 1) s.rows_per_wave = 1;
+  s.staged = per_mod >= kWavesPerBlock * s.rows_per_wave;
+  if (!s.staged) s.rows_per_wave = 1;
+#ifdef DIT_TUNING
+  if (getenv("DIT_NO_STAGING")) {
+    s.staged = false;
+    s.rows_per_wave = 1;
+  }
+#endif
+  const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
+  s.grid = dim3((unsigned)((rows + wg_rows - 1) / wg_rows));
+  return s;
 }
 
 #define DIT_NC_CASES(X) \
   X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 
+// Selects the instantiation NC = ceil(dim / 512) through the X macro in scope.
+#define DIT_ROW_DISPATCH()                      \
+  do {                                          \
+    switch ((int)((a.dim + 511) / 512)) {       \
+      DIT_NC_CASES(X)                           \
+      default: return hipErrorInvalidValue;     \
+    }                                           \
+    return hipGetLastError();                   \
+  } while (0)
+
+// LDS bytes of `rows` staged rows of NC vectors each.
+static size_t lds_bytes(int64_t dim, int rows) {
+  return (size_t)rows * (size_t)((dim + 511) / 512) * 64 * sizeof(uint4);
+}
+
 template <int MODE>
-static hipError_t ln_dispatch(const LnModArgs &a, hipStream_t s) {
-  const int nc = (int)((a.dim + 511) / 512);
-  switch (nc) {
-#define X(N) \
-  case N:    \
-    hipLaunchKernelGGL((k_ln_modulate<N, MODE>), row_grid(a.rows), dim3(256), 0, s, a); break;
-    DIT_NC_CASES(X)
+static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod);
+  a.rows_per_wave = sh.rows_per_wave;
+  const size_t shm = sh.staged ? lds_bytes(a.dim, 4) : 0;
+#define X(N)                                                                          \
+  case N:                                                                             \
+    if (sh.staged)                                                                    \
+      DIT_LAUNCH((k_ln_modulate<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
+    else                                                                              \
+      DIT_LAUNCH((k_ln_modulate<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a);  \
+    break;
+  DIT_ROW_DISPATCH();
 #undef X
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod);
+  a.rows_per_wave = sh.rows_per_wave;
+  const size_t shm = sh.staged ? lds_bytes(a.dim, 3) : 0;
+#define X(N)                                                                            \
+  case N:                                                                               \
+    if (sh.staged)                                                                      \
+      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
+    else                                                                                \
+      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a);  \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
+}
+
+template <int MODE>
+static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod);
+  a.rows_per_wave = sh.rows_per_wave;
+  const size_t shm = sh.staged ? lds_bytes(a.dim, 3) : 0;
+#define X(N)                                                                                  \
+  case N:                                                                                     \
+    if (sh.staged)                                                                            \
+      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, \
+                 a);                                                                          \
+    else                                                                                      \
+      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, false>), sh.grid, dim3(kThreads), 0, s,  \
+                 a);                                                                          \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
+}
+
+static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod);
+  a.rows_per_wave = sh.rows_per_wave;
+  const size_t shm = sh.staged ? lds_bytes(a.dim, 2) : 0;
+#define X(N)                                                                              \
+  case N:                                                                                 \
+    if (sh.staged)                                                                        \
+      DIT_LAUNCH((k_residual_gate_add<N, true>), sh.grid, dim3(kThreads), shm, s, a);    \
+    else                                                                                  \
+      DIT_LAUNCH((k_residual_gate_add<N, false>), sh.grid, dim3(kThreads), 0, s, a);     \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
 }
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s) {
   return mode == kFast ? ln_dispatch<kFast>(a, s) : ln_dispatch<kLossless>(a, s);
 }
 
-template <int MODE>
-static hipError_t rms_scale_dispatch(const RmsScaleArgs &a, hipStream_t s) {
-  const int nc = (int)((a.dim + 511) / 512);
-  switch (nc) {
-#define X(N) \
-  case N:    \
-    hipLaunchKernelGGL((k_rmsnorm_scale<N, MODE>), row_grid(a.rows), dim3(256), 0, s, a); break;
-    DIT_NC_CASES(X)
-#undef X
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s) {
   return mode == kFast ? rms_scale_dispatch<kFast>(a, s) : rms_scale_dispatch<kLossless>(a, s);
-}
-
-template <int MODE>
-static hipError_t rms_tanh_dispatch(const RmsTanhArgs &a, hipStream_t s) {
-  const int nc = (int)((a.dim + 511) / 512);
-  switch (nc) {
-#define X(N)                                                                             \
-  case N:                                                                                \
-    hipLaunchKernelGGL((k_rmsnorm_tanh_residual<N, MODE>), row_grid(a.rows), dim3(256), 0, \
-                       s, a);                                                            \
-    break;
-    DIT_NC_CASES(X)
-#undef X
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStream_t s) {
@@ -303,16 +532,7 @@ hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStrea
 }
 
 hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t s) {
-  const int nc = (int)((a.dim + 511) / 512);
-  switch (nc) {
-#define X(N) \
-  case N:    \
-    hipLaunchKernelGGL((k_residual_gate_add<N>), row_grid(a.rows), dim3(256), 0, s, a); break;
-    DIT_NC_CASES(X)
-#undef X
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return gate_add_dispatch(a, s);
 }
 
 }  // namespace dit
