@@ -1,0 +1,220 @@
+"""CPU tests of the C ABI: the built library exports every declared entry point,
+and the host guards accept, reject and forward arguments as documented.
+
+The guard tests link the real ABI layer (csrc/dit_abi.cpp) with stand-in
+launchers (tests/host_stub.cpp) that record the launch instead of running it,
+so no GPU is touched.  Pointers are fake, 16-byte aligned addresses.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+CSRC = os.path.join(ROOT, "modulation_bf16_row_amd", "csrc")
+LIB = os.path.join(ROOT, "modulation_bf16_row_amd", "libdit.so")
+
+OK, UNSUPPORTED, INVALID, HIP = 0, 1, 2, 3
+vp, i64, f32, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(INCLUDE):
+        if fn.endswith(".h"):
+            text = open(os.path.join(INCLUDE, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(dit_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    if not os.path.exists(LIB):
+        pytest.skip("libdit.so not built")
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 12
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    lib.dit_abi_version.restype = cint
+    assert lib.dit_abi_version() == 1
+
+
+@pytest.fixture(scope="module")
+def stub(tmp_path_factory):
+    d = tmp_path_factory.mktemp("stub")
+    so = str(d / "libdit_hoststub.so")
+    cmd = ["/opt/rocm/bin/hipcc", "-std=c++17", "-O1", "-fPIC", "-shared",
+           "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, "dit_abi.cpp"), os.path.join(ROOT, "tests", "host_stub.cpp"),
+           "-o", so]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    lib = ctypes.CDLL(so)
+    lib.dit_status_reason.restype = ctypes.c_char_p
+    lib.dit_ln_modulate.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, f32, cint, vp]
+    lib.dit_rmsnorm_scale.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, f32, cint,
+                                      vp]
+    lib.dit_rmsnorm_tanh_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64,
+                                              i64, f32, cint, vp]
+    lib.dit_residual_gate_add.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint,
+                                          vp]
+    return lib
+
+
+class Rec:
+    def __init__(self, lib):
+        self.lib = lib
+
+    @property
+    def calls(self):
+        return ctypes.c_int.in_dll(self.lib, "stub_calls").value
+
+    @property
+    def name(self):
+        return ctypes.c_char_p(ctypes.addressof(ctypes.c_char.in_dll(self.lib, "stub_name"))
+                               ).value.decode()
+
+    @property
+    def vals(self):
+        return list((ctypes.c_int64 * 16).in_dll(self.lib, "stub_vals"))
+
+
+A = 1 << 20          # fake device addresses, far apart and 16-byte aligned
+X, OUT, SC, SH, W, RES, Y, G = (A * k for k in range(1, 9))
+
+
+def ln(lib, out=OUT, out_rs=1024, x=X, x_rs=1024, sc=SC, sh=SH, mod_rs=1024, mod_rows=1,
+       rows=8, dim=1024, mode=0):
+    return lib.dit_ln_modulate(out, out_rs, x, x_rs, sc, sh, mod_rs, mod_rows, rows, dim,
+                               1e-6, mode, None)
+
+
+def test_ln_accepts_and_forwards(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert ln(stub, rows=12, mod_rows=3, x_rs=1536, out_rs=2048) == OK
+    assert r.calls == n0 + 1 and r.name == "ln_modulate"
+    assert r.vals[:6] == [12, 1024, 4, 2048, 1536, 1024]     # rows, dim, per_mod, strides
+    assert ln(stub, out=X, out_rs=1024) == OK                   # exact in-place
+
+
+@pytest.mark.parametrize("kw,status,why", [
+    (dict(mode=2), INVALID, "mode"),
+    (dict(rows=-1), INVALID, "negative"),
+    (dict(dim=8200), UNSUPPORTED, "8192"),
+    (dict(dim=1020), UNSUPPORTED, "% 8"),
+    (dict(dim=0), UNSUPPORTED, "dim == 0"),
+    (dict(rows=8, mod_rows=3), UNSUPPORTED, "mod_rows"),
+    (dict(mod_rows=0), INVALID, "mod_rows == 0"),
+    (dict(x=0), INVALID, "NULL"),
+    (dict(sh=0), INVALID, "NULL"),
+    (dict(x_rs=1000), UNSUPPORTED, "stride"),
+    (dict(x_rs=1028), UNSUPPORTED, "stride"),
+    (dict(x=X + 8), UNSUPPORTED, "aligned"),
+    (dict(out=X + 2048, out_rs=1024), INVALID, "overlap"),       # out one row below x
+    (dict(out=X, out_rs=2048, x_rs=2048 + 8), INVALID, "overlap"),
+    (dict(out=SC), INVALID, "overlap"),                          # writes the modulation
+])
+def test_ln_rejections_touch_nothing(stub, kw, status, why):
+    r = Rec(stub)
+    n0 = r.calls
+    assert ln(stub, **kw) == status
+    assert r.calls == n0, "a rejected call must not launch"
+    assert why.lower() in stub.dit_status_reason().decode().lower()
+
+
+def test_empty_problem_is_ok_without_launch(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert ln(stub, rows=0, x=0, out=0) == OK
+    assert r.calls == n0
+
+
+def test_interleaved_views_in_one_buffer_are_not_overlap(stub):
+    """x = columns [0, 1024) and out = columns [1024, 2048) of one [8, 2048]
+    buffer share rows but no element."""
+    assert ln(stub, x=X, x_rs=2048, out=X + 2048, out_rs=2048) == OK
+    # ... but shifted by 512 columns they do overlap
+    assert ln(stub, x=X, x_rs=2048, out=X + 1024, out_rs=2048) == INVALID
+
+
+def test_other_row_ops(stub):
+    r = Rec(stub)
+    assert stub.dit_rmsnorm_scale(OUT, 3072, X, 3072, W, SC, 3072, 2, 10, 3072, 1e-6, 1,
+                                  None) == OK
+    assert r.name == "rmsnorm_scale" and r.vals[:3] == [10, 3072, 5]
+    assert stub.dit_rmsnorm_scale(OUT, 3072, X, 3072, OUT, SC, 3072, 2, 10, 3072, 1e-6, 0,
+                                  None) == INVALID                # out overwrites weight
+    assert stub.dit_rmsnorm_tanh_residual(RES, 3072, X, 3072, RES, 3072, W, G, 3072, 10, 10,
+                                          3072, 1e-6, 0, None) == OK   # in place on residual
+    assert r.name == "rmsnorm_tanh_residual" and r.vals[2] == 1
+    assert stub.dit_residual_gate_add(OUT, 512, RES, 512, Y, 512, G, 512, 1, 4, 512, 5,
+                                      None) == INVALID            # bad mode
+    assert stub.dit_residual_gate_add(OUT, 512, RES, 512, Y, 512, G, 512, 1, 4, 512, 0,
+                                      None) == OK
+    assert r.name == "residual_gate_add" and r.vals[:3] == [4, 512, 4]
+
+
+class Stream(ctypes.Structure):
+    _fields_ = [("q", vp), ("k", vp), ("v", vp), ("tok_stride", i64), ("batch_stride", i64),
+                ("q_weight", vp), ("k_weight", vp), ("tokens", i64)]
+
+
+def _qkv(lib, txt, img, qo, ko, vo, ots, obs, batch=2, heads=24, hd=128, cos=A * 40,
+         sin=A * 44, mode=0):
+    lib.dit_qk_norm_rope.argtypes = [vp, vp, vp, i64, i64, ctypes.POINTER(Stream),
+                                     ctypes.POINTER(Stream), vp, vp, i64, i64, i64, f32, cint, vp]
+    return lib.dit_qk_norm_rope(qo, ko, vo, ots, obs, ctypes.byref(txt) if txt else None,
+                                ctypes.byref(img) if img else None, cos, sin, batch, heads, hd,
+                                1e-6, mode, None)
+
+
+def _streams():
+    H, Dh = 24, 128
+    W3 = 3 * H * Dh
+    img_base, txt_base = A * 64, A * 256
+    img = Stream(img_base, img_base + 2 * H * Dh, img_base + 4 * H * Dh, W3, 4096 * W3,
+                 A * 48, A * 49, 4096)
+    txt = Stream(txt_base, txt_base + 2 * H * Dh, txt_base + 4 * H * Dh, W3, 512 * W3,
+                 A * 50, A * 51, 512)
+    return txt, img
+
+
+def test_qkv_guards(stub):
+    r = Rec(stub)
+    txt, img = _streams()
+    H, Dh, S = 24, 128, 4608
+    base = A * 512
+    # separate contiguous outputs
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh) == OK
+    assert r.name == "qk_norm_rope" and r.vals[:7] == [2, 24, 4608, 3072, S * 3072, 512, 4096]
+    # one interleaved [B, S, 3, H, Dh] buffer
+    assert _qkv(stub, txt, img, base, base + 2 * H * Dh, base + 4 * H * Dh, 3 * H * Dh,
+                S * 3 * H * Dh) == OK
+    # outputs overlapping each other
+    assert _qkv(stub, txt, img, base, base + 2 * 1024, base + 4 * H * Dh, 3 * H * Dh,
+                S * 3 * H * Dh) == INVALID
+    # output over an input stream
+    assert _qkv(stub, txt, img, txt.q, base + A * 64, base + A * 128, H * Dh, S * H * Dh) \
+        == INVALID
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                hd=64) == UNSUPPORTED
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                heads=65) == UNSUPPORTED
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                mode=7) == INVALID
+    # empty problems launch nothing
+    n0 = r.calls
+    assert _qkv(stub, None, None, 0, 0, 0, 0, 0) == OK
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                batch=0) == OK
+    assert r.calls == n0
+    # text-only
+    assert _qkv(stub, txt, None, base, base + A * 64, base + A * 128, H * Dh, 512 * H * Dh) == OK
+    # misaligned table
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                cos=A * 40 + 4) == UNSUPPORTED
