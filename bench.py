@@ -12,16 +12,20 @@ of 128), all in LOSSLESS mode:
 
 Inputs are resident in HBM before timing.  Two complete buffer sets are
 alternated step by step so that every kernel's operands were last touched
-about 1.4 GB of traffic earlier: the 256 MB Infinity Cache cannot serve them.
-Per-kernel durations come from HIP events recorded on the launch stream.
+about 0.9 GB of traffic earlier: the 256 MB Infinity Cache cannot serve them.
+Per-kernel durations come from HIP events that the kernel dispatches record
+themselves (dit_time_next_launch), on the launch stream.
 
-value = algorithmic bytes of one step / time per step (GB/s, whole job).
-The roofline object reports LN + AdaLN modulate, the kernel the metric names.
+value = algorithmic bytes of one step / time per step (GB/s, whole job).  The
+timed steps replay one HIP graph per buffer set (captured from the same five
+calls), so host launch cost does not leave the GPU idle between kernels.
+The roofline object reports LN + AdaLN modulate, the kernel the metric
+names; per-kernel durations come from K further steps launched eagerly from
+prepared calls, each dispatch recording its own start/stop events.
 The CPU baseline runs the oracle (plain C, one thread) over one full step on
 the host and also compares its outputs with the GPU's, bit for bit.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -47,16 +51,13 @@ BYTES = {
     "residual_gate_add": 3 * ROWS * D * 2 + B * D * 2,               # res, y, out; gate
     "qk_norm_rope": 2 * 3 * ROWS * H * DH * 2 + 4 * DH * 2 + 2 * (S_IMG + S_TXT) * (DH // 2) * 4,
 }
-KERNELS = list(BYTES)
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "modulation_bf16_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+# Step order as in a DiT block: the previous sublayer's gate-add, then the next
+# norm + modulate, the QKV epilogue, and the RMSNorm variants.  (A kernel
+# that follows another pays part of its predecessor's write drain, so
+# per-kernel durations depend on the order; the step total does not.)
+KERNELS = ["residual_gate_add", "ln_modulate", "qk_norm_rope", "rmsnorm_scale",
+           "rmsnorm_tanh_residual"]
+ROW_KERNELS = [k for k in KERNELS if k != "qk_norm_rope"]   # (rows, D) outputs
 
 
 def read_traffic(kernel):
@@ -71,6 +72,7 @@ def read_traffic(kernel):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
+    from modulation_bf16_row_amd.profiling import kernel_source_hash
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
@@ -102,7 +104,7 @@ class BufferSet:
         self.scale2 = to_dev(blk["scale2"], torch)
         self.w = to_dev(blk["weight"], torch)
         self.out = {k: torch.empty((ROWS, D), dtype=torch.bfloat16, device="cuda")
-                    for k in KERNELS[:4]}
+                    for k in ROW_KERNELS}
         img = to_dev(qkv["img_qkv"], torch)
         txt = to_dev(qkv["txt_qkv"], torch)
         self._keep = (img, txt)
@@ -122,23 +124,29 @@ class BufferSet:
                                          device="cuda") for _ in range(3))
 
 
-def run_step(m, s, mode, ev=None):
-    """Launches the five epilogues.  With ev, ev[k] = (start, stop) HIP events
-    that the dispatch of kernel k records itself (dit_time_next_launch)."""
-    def timed(k):
-        if ev is not None:
-            m.dit_time_next_launch(ev[k][0], ev[k][1])
-    timed("ln_modulate")
-    m.dit_ln_modulate(s.x, s.scale, s.shift, EPS, mode, out=s.out["ln_modulate"])
-    timed("rmsnorm_scale")
-    m.dit_rmsnorm_scale(s.x, s.w, s.scale2, EPS, mode, out=s.out["rmsnorm_scale"])
-    timed("rmsnorm_tanh_residual")
-    m.dit_rmsnorm_tanh_residual(s.x, s.res, s.w, s.gate, EPS, mode,
-                                out=s.out["rmsnorm_tanh_residual"])
-    timed("residual_gate_add")
-    m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.out["residual_gate_add"])
-    timed("qk_norm_rope")
-    m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode, out=s.qkv_out)
+def run_step(m, s, mode):
+    """Launches the five epilogues on the current stream, in KERNELS order."""
+    plans = make_plans(m, s, mode)
+    for k in KERNELS:
+        plans[k]()
+
+
+def make_plans(m, s, mode):
+    """The five calls of one step, marshalled once (launch = one C call)."""
+    return {
+        "ln_modulate": m.dit_ln_modulate(s.x, s.scale, s.shift, EPS, mode,
+                                         out=s.out["ln_modulate"], prepare=True),
+        "rmsnorm_scale": m.dit_rmsnorm_scale(s.x, s.w, s.scale2, EPS, mode,
+                                             out=s.out["rmsnorm_scale"], prepare=True),
+        "rmsnorm_tanh_residual": m.dit_rmsnorm_tanh_residual(
+            s.x, s.res, s.w, s.gate, EPS, mode, out=s.out["rmsnorm_tanh_residual"],
+            prepare=True),
+        "residual_gate_add": m.dit_residual_gate_add(s.res, s.y, s.gate, mode,
+                                                     out=s.out["residual_gate_add"],
+                                                     prepare=True),
+        "qk_norm_rope": m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode,
+                                           out=s.qkv_out, prepare=True),
+    }
 
 
 def cpu_baseline(blk, qkv, gpu_out):
@@ -174,7 +182,7 @@ def cpu_baseline(blk, qkv, gpu_out):
     t_ops["qk_norm_rope"] = time.perf_counter() - t0
     total_t = sum(t_ops.values())
     exact = {}
-    for k in KERNELS[:4]:
+    for k in ROW_KERNELS:
         exact[k] = bool(np.array_equal(gpu_out[k], refs[k]))
     exact["qk_norm_rope"] = all(np.array_equal(g, r) for g, r in zip(gpu_out["qk_norm_rope"],
                                                                      refs["qk_norm_rope"]))
@@ -185,20 +193,25 @@ def cpu_baseline(blk, qkv, gpu_out):
                 seconds_per_op={k: round(v, 3) for k, v in t_ops.items()}), exact
 
 
-def copy_ceiling(torch, nbytes=1 << 30, reps=5):
-    """Practical HBM ceiling: torch's device copy of a 1 GiB bf16 buffer (2 GiB
-    moved per copy, far beyond the Infinity Cache), GB/s of read + write."""
+def copy_ceiling(m, torch, nbytes=1 << 30, reps=5):
+    """Practical HBM ceiling: the library's streaming-copy probe (128-bit
+    accesses, nontemporal loads and stores) over a 1 GiB buffer, 2 GiB moved
+    per copy, far beyond the Infinity Cache; GB/s of read + write.  These
+    dispatches of known size also calibrate the memory counters."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m.dit_probe_copy(dst, src, 3)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        b.record()
     torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e.record()
+    for a, b in evs:
+        m.dit_time_next_launch(a, b)
+        m.dit_probe_copy(dst, src, 3)
     torch.cuda.synchronize()
-    sec = s.elapsed_time(e) * 1e-3 / reps
+    sec = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
     del src, dst
     return round(2 * nbytes / sec / 1e9, 1)
 
@@ -229,22 +242,50 @@ def main():
         run_step(m, sets[i % 2], args.mode)
     torch.cuda.synchronize()
 
+    # One HIP graph per buffer set, captured from the same five calls: the
+    # timed steps replay them, so host launch cost does not gap the GPU.
+    graphs = []
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(m, s, args.mode)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        graphs[i % 2].replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # Per-kernel durations: K more steps launched eagerly from prepared calls,
+    # each dispatch recording its own start/stop events.
+    plans = [make_plans(m, s, args.mode) for s in sets]
     ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
               for _ in range(args.steps)] for k in KERNELS}
     for k in KERNELS:                  # record once so the HIP events exist
         for pair in ev[k]:
             for e in pair:
                 e.record()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
+    e0.record()
     for i in range(args.steps):
-        run_step(m, sets[i % 2], args.mode, {k: ev[k][i] for k in KERNELS})
-    end.record()
+        p = plans[i % 2]
+        for k in KERNELS:
+            m.dit_time_next_launch(*ev[k][i])
+            p[k]()
+    e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(end) / args.steps
+    eager_ms_step = e0.elapsed_time(e1) / args.steps
     k_us = {k: 1000.0 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev[k]]))
             for k in KERNELS}
 
@@ -268,14 +309,16 @@ def main():
                              "RMSNorm-scale, RMSNorm-tanh-residual, residual gate-add, "
                              "Q/K RMSNorm+RoPE+joint QKV)",
                     batch=B, tokens=S_IMG + S_TXT, hidden=D, heads=H, head_dim=DH,
-                    mode=args.mode, step_bytes=step_bytes, host_wall_ms_per_step=round(
-                        1000 * wall / args.steps, 4)),
+                    mode=args.mode, step_bytes=step_bytes, launch="hip graph replay",
+                    host_wall_ms_per_step=round(1000 * wall / args.steps, 4)),
         roofline=roofline, kernels=per_kernel,
-        copy_ceiling_gbs=copy_ceiling(torch),
+        eager_ms_per_step=round(eager_ms_step, 4),
+        kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
+        copy_ceiling_gbs=copy_ceiling(m, torch),
     )
     if not args.no_cpu:
         gpu_out = {k: sets[0].out[k].cpu().view(torch.int16).numpy().view(np.uint16)
-                   for k in KERNELS[:4]}
+                   for k in ROW_KERNELS}
         gpu_out["qk_norm_rope"] = [t.cpu().view(torch.int16).numpy().view(np.uint16)
                                    for t in sets[0].qkv_out]
         base, exact = cpu_baseline(blk, qkv, gpu_out)

@@ -46,6 +46,14 @@ dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, i
 dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
                                hipStream_t stream);
 
+/* Streaming copy of `bytes` (a multiple of 16; 16-byte aligned, non-overlapping
+ * buffers) with the epilogues' access pattern: 128-bit accesses, 1 KiB
+ * contiguous per wave instruction.  Used as the practical HBM ceiling and to
+ * calibrate memory counters.  flags bit 0: nontemporal loads; bit 1:
+ * nontemporal stores. */
+dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

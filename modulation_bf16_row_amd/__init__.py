@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     FAST, LOSSLESS, DitError, DitHipError, DitInvalid, DitUnsupported, LIB_PATH, lib,
     dit_ln_modulate, dit_qk_norm_rope, dit_residual_gate_add, dit_rmsnorm_scale,
     dit_rmsnorm_tanh_residual, dit_probe_bf16_round, dit_probe_f32, dit_probe_row_sum,
-    dit_probe_unary, dit_time_next_launch,
+    dit_probe_unary, dit_probe_copy, dit_time_next_launch,
 )

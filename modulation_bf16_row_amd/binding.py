@@ -68,6 +68,7 @@ SIGNATURES = {
     "dit_probe_f32": [_int, _vp, _vp, _vp, _i64, _int, _vp],
     "dit_probe_row_sum": [_vp, _vp, _i64, _i64, _int, _vp],
     "dit_time_next_launch": [_vp, _vp],
+    "dit_probe_copy": [_vp, _vp, _i64, _int, _vp],
 }
 
 
@@ -164,8 +165,36 @@ def _mod_rows(a, b, dim, names):
     return ra, sa
 
 
-def dit_ln_modulate(x, scale, shift, eps=1e-6, mode="lossless", out=None):
-    """LN(x) * (1 + scale) + shift with the lossless rounding contract."""
+class PreparedCall:
+    """A fully marshalled epilogue call: checks and argument conversion were
+    done once, on the stream that was current then; calling it only enqueues
+    the kernel (one C call).  Returns the output tensor(s)."""
+    __slots__ = ("_fn", "_args", "_result")
+
+    def __init__(self, fn, args, result):
+        self._fn, self._args, self._result = fn, args, result
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status:
+            _check(status)
+        return self._result
+
+
+def _call(name, result, prepare, *args):
+    fn = getattr(lib(), name)
+    if prepare:
+        conv = tuple(t(a) if not isinstance(a, (ctypes._SimpleCData, ctypes.Structure,
+                                                 ctypes._Pointer)) and t is not None else a
+                     for a, t in zip(args, SIGNATURES[name]))
+        return PreparedCall(fn, conv, result)
+    _check(fn(*args))
+    return result
+
+
+def dit_ln_modulate(x, scale, shift, eps=1e-6, mode="lossless", out=None, prepare=False):
+    """LN(x) * (1 + scale) + shift with the lossless rounding contract.
+    With prepare=True, returns a PreparedCall instead of launching."""
     _same_device(x, scale, shift)
     rows, x_rs = _flat_rows(x, "x")
     dim = x.shape[-1]
@@ -173,13 +202,12 @@ def dit_ln_modulate(x, scale, shift, eps=1e-6, mode="lossless", out=None):
     out = _out_like(x, out)
     _same_device(x, out)
     _, o_rs = _flat_rows(out, "out")
-    _check(lib().dit_ln_modulate(out.data_ptr(), o_rs, x.data_ptr(), x_rs, scale.data_ptr(),
-                                 shift.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
-                                 _stream(x)))
-    return out
+    return _call("dit_ln_modulate", out, prepare, out.data_ptr(), o_rs, x.data_ptr(), x_rs,
+                 scale.data_ptr(), shift.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
+                 _stream(x))
 
 
-def dit_rmsnorm_scale(x, weight, scale, eps=1e-6, mode="lossless", out=None):
+def dit_rmsnorm_scale(x, weight, scale, eps=1e-6, mode="lossless", out=None, prepare=False):
     _same_device(x, weight, scale)
     rows, x_rs = _flat_rows(x, "x")
     dim = x.shape[-1]
@@ -189,13 +217,13 @@ def dit_rmsnorm_scale(x, weight, scale, eps=1e-6, mode="lossless", out=None):
     out = _out_like(x, out)
     _same_device(x, out)
     _, o_rs = _flat_rows(out, "out")
-    _check(lib().dit_rmsnorm_scale(out.data_ptr(), o_rs, x.data_ptr(), x_rs, weight.data_ptr(),
-                                   scale.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
-                                   _stream(x)))
-    return out
+    return _call("dit_rmsnorm_scale", out, prepare, out.data_ptr(), o_rs, x.data_ptr(), x_rs,
+                 weight.data_ptr(), scale.data_ptr(), mrs, mrows, rows, dim, eps, _mode(mode),
+                 _stream(x))
 
 
-def dit_rmsnorm_tanh_residual(x, residual, weight, gate, eps=1e-6, mode="lossless", out=None):
+def dit_rmsnorm_tanh_residual(x, residual, weight, gate, eps=1e-6, mode="lossless", out=None,
+                              prepare=False):
     _same_device(x, residual, weight, gate)
     rows, x_rs = _flat_rows(x, "x")
     dim = x.shape[-1]
@@ -208,14 +236,12 @@ def dit_rmsnorm_tanh_residual(x, residual, weight, gate, eps=1e-6, mode="lossles
     out = _out_like(x, out)
     _same_device(x, out)
     _, o_rs = _flat_rows(out, "out")
-    _check(lib().dit_rmsnorm_tanh_residual(out.data_ptr(), o_rs, x.data_ptr(), x_rs,
-                                           residual.data_ptr(), r_rs, weight.data_ptr(),
-                                           gate.data_ptr(), mrs, mrows, rows, dim, eps,
-                                           _mode(mode), _stream(x)))
-    return out
+    return _call("dit_rmsnorm_tanh_residual", out, prepare, out.data_ptr(), o_rs, x.data_ptr(),
+                 x_rs, residual.data_ptr(), r_rs, weight.data_ptr(), gate.data_ptr(), mrs, mrows,
+                 rows, dim, eps, _mode(mode), _stream(x))
 
 
-def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None):
+def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None, prepare=False):
     _same_device(residual, y, gate)
     rows, r_rs = _flat_rows(residual, "residual")
     dim = residual.shape[-1]
@@ -226,10 +252,9 @@ def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None):
     out = _out_like(residual, out)
     _same_device(residual, out)
     _, o_rs = _flat_rows(out, "out")
-    _check(lib().dit_residual_gate_add(out.data_ptr(), o_rs, residual.data_ptr(), r_rs,
-                                       y.data_ptr(), y_rs, gate.data_ptr(), mrs, mrows, rows,
-                                       dim, _mode(mode), _stream(residual)))
-    return out
+    return _call("dit_residual_gate_add", out, prepare, out.data_ptr(), o_rs, residual.data_ptr(),
+                 r_rs, y.data_ptr(), y_rs, gate.data_ptr(), mrs, mrows, rows, dim, _mode(mode),
+                 _stream(residual))
 
 
 def _qkv_stream(st):
@@ -254,10 +279,11 @@ def _qkv_stream(st):
     return s, tuple(q.shape)
 
 
-def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None):
+def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None, prepare=False):
     """Q/K RMSNorm + interleaved RoPE + V copy into joint [B, S_txt + S_img, H, Dh]
     outputs (text tokens first).  ``out`` may be a (q, k, v) triple of views
-    sharing token and batch strides."""
+    sharing token and batch strides.  With prepare=True, returns a
+    PreparedCall instead of launching."""
     ts, tshape = _qkv_stream(txt)
     is_, ishape = _qkv_stream(img)
     ref = img["q"] if img is not None else txt["q"]
@@ -280,11 +306,9 @@ def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None):
             raise DitInvalid("outputs must be bfloat16 [B, S_txt + S_img, H, Dh]")
         if t.stride(3) != 1 or t.stride(2) != Dh or t.stride() != qo.stride():
             raise DitUnsupported("outputs must share strides with packed heads")
-    _check(lib().dit_qk_norm_rope(qo.data_ptr(), ko.data_ptr(), vo.data_ptr(), qo.stride(1),
-                                  qo.stride(0), ctypes.byref(ts), ctypes.byref(is_),
-                                  cos.data_ptr(), sin.data_ptr(), B, H, Dh, eps, _mode(mode),
-                                  _stream(ref)))
-    return out
+    return _call("dit_qk_norm_rope", out, prepare, qo.data_ptr(), ko.data_ptr(), vo.data_ptr(),
+                 qo.stride(1), qo.stride(0), ctypes.pointer(ts), ctypes.pointer(is_),
+                 cos.data_ptr(), sin.data_ptr(), B, H, Dh, eps, _mode(mode), _stream(ref))
 
 
 def dit_time_next_launch(start, stop):
@@ -317,6 +341,15 @@ def dit_probe_f32(op, a, b=None, mode="lossless"):
                                b.data_ptr() if b is not None else None, a.numel(), _mode(mode),
                                _stream(a)))
     return out
+
+
+def dit_probe_copy(dst, src, flags=0):
+    """Streaming device copy of src into dst (same number of bytes)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise DitInvalid("dst and src sizes differ")
+    _check(lib().dit_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, flags, _stream(src)))
+    return dst
 
 
 def dit_probe_row_sum(t, head=False):

@@ -394,6 +394,20 @@ dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, i
   return hip_status(dit::launch_probe_f32(op, out, a, b, n, mode, stream));
 }
 
+dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
+                            hipStream_t stream) {
+  if (bytes < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (flags < 0 || flags > 3) return fail(DIT_ERR_INVALID, "flags must be in [0, 3]");
+  if (bytes == 0) return DIT_OK;
+  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (bytes % 16 != 0 || !aligned16(out) || !aligned16(in))
+    return fail(DIT_ERR_UNSUPPORTED, "bytes and pointers must be multiples of 16");
+  if (spans_overlap(Span{reinterpret_cast<uintptr_t>(out), 0, 1, bytes},
+                    Span{reinterpret_cast<uintptr_t>(in), 0, 1, bytes}))
+    return fail(DIT_ERR_INVALID, "buffers overlap");
+  return hip_status(dit::launch_probe_copy(out, in, bytes / 16, flags, stream));
+}
+
 dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
                                hipStream_t stream) {
   if (rows < 0 || dim < 0) return fail(DIT_ERR_INVALID, "negative size");

@@ -90,5 +90,6 @@ hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, 
                             int mode, hipStream_t s);
 hipError_t launch_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
                                 hipStream_t s);
+hipError_t launch_probe_copy(void *out, const void *in, int64_t n16, int flags, hipStream_t s);
 
 }  // namespace dit

@@ -71,7 +71,48 @@ __global__ __launch_bounds__(64) void k_probe_row_sum(float *out, const float *t
   }
 }
 
+// Streaming copy of n 16-byte vectors with the epilogues' access pattern (each
+// wave moves 1 KiB contiguous per instruction): the practical HBM ceiling.
+// FLAGS bit 0: nontemporal loads; bit 1: nontemporal stores.
+template <int FLAGS>
+__global__ __launch_bounds__(256) void k_probe_copy(u32x4 *out, const u32x4 *in, int64_t n) {
+  const int64_t step = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x; base < n; base += step) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = base + 256 * k;
+      if (i < n) v[k] = (FLAGS & 1) ? __builtin_nontemporal_load(in + i) : in[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = base + 256 * k;
+      if (i < n) {
+        if (FLAGS & 2)
+          __builtin_nontemporal_store(v[k], out + i);
+        else
+          out[i] = v[k];
+      }
+    }
+  }
+}
+
 static dim3 flat_grid(int64_t n, int block) { return dim3((unsigned)((n + block - 1) / block)); }
+
+hipError_t launch_probe_copy(void *out, const void *in, int64_t n16, int flags, hipStream_t s) {
+  int64_t blocks = (n16 + 1023) / 1024;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  const dim3 grid((unsigned)blocks);
+  u32x4 *o = static_cast<u32x4 *>(out);
+  const u32x4 *i = static_cast<const u32x4 *>(in);
+  switch (flags & 3) {
+    case 0: DIT_LAUNCH(k_probe_copy<0>, grid, dim3(256), 0, s, o, i, n16); break;
+    case 1: DIT_LAUNCH(k_probe_copy<1>, grid, dim3(256), 0, s, o, i, n16); break;
+    case 2: DIT_LAUNCH(k_probe_copy<2>, grid, dim3(256), 0, s, o, i, n16); break;
+    default: DIT_LAUNCH(k_probe_copy<3>, grid, dim3(256), 0, s, o, i, n16); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t s) {
   DIT_LAUNCH(k_probe_bf16_round, flat_grid(n, 256), dim3(256), 0, s, out, in, n);

@@ -4,8 +4,8 @@
 // "基于Agent的SGLang扩散模型Kernel优化实践", section "合并QKV投影时的数值问题").
 //
 // Geometry: a 64-lane wave handles one (batch, joint token) at a time and
-// walks a contiguous run of `tokens_per_wave` of them, sized so that all
-// waves are resident at once (no tail round).  Within a token the wave covers four heads at
+// walks a contiguous run of `tokens_per_wave` of them (one, unless the
+// problem is huge).  Within a token the wave covers four heads at
 // a time: lanes 16g..16g+15 hold head 4i+g, each lane 8 elements (128-bit
 // access), so a wave-wide access is 1 KiB of the token's row.  Each lane's
 // four RoPE pairs (4r .. 4r+3 for r = lane % 16) have their cos/sin loaded
@@ -79,9 +79,9 @@ __device__ __forceinline__ void load_token(Token<HG> &t, const QkvArgs &a, int64
   for (int i = 0; i < HG; ++i) {
     const int h = 4 * i + g;
     if (h < a.heads) {
-      t.q[i] = load8(st.q + src + h * kHeadDim);
-      t.k[i] = load8(st.k + src + h * kHeadDim);
-      t.v[i] = load8(st.v + src + h * kHeadDim);
+      t.q[i] = load8_stream(st.q + src + h * kHeadDim);
+      t.k[i] = load8_stream(st.k + src + h * kHeadDim);
+      t.v[i] = load8_stream(st.v + src + h * kHeadDim);
     }
   }
   t.wq = load8(st.q_weight + 8 * r);
@@ -124,8 +124,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
 }
 
-// About kQkvTargetWaves waves in flight (MI355X: 256 CUs x 4 SIMDs x 4).
-constexpr int64_t kQkvTargetWaves = 4096;
+// One token per wave measured fastest at the Qwen-Image shape (9216 tokens);
+// runs only start above ~1M tokens, to bound the grid.
+constexpr int64_t kQkvTargetWaves = int64_t(1) << 20;
 
 template <int MODE>
 static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {

@@ -6,7 +6,9 @@
 // wave walks a contiguous run of `rows_per_wave` rows; a 256-thread
 // workgroup (four waves) covers 4 * rows_per_wave consecutive rows.  The
 // row stays in VGPRs between the LayerNorm passes, so x is read from HBM
-// once; latency is hidden by the other waves resident on the SIMD.
+// once; latency is hidden by the other waves resident on the SIMD.  Rows
+// and outputs move with the nontemporal cache policy; shared operands with
+// the default one.
 //
 // Modulation operands.  With per-batch modulation (a workgroup's rows meet
 // at most two modulation rows), the workgroup computes the per-element
@@ -33,10 +35,19 @@ namespace dit {
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 64 * kWavesPerBlock;
 
+// Load policy of the streamed row inputs, per kernel, as measured on MI355X
+// (Qwen-Image and Wan shapes): the nontemporal policy helps the kernels that
+// read two or more row streams and slows the single-stream norms.
+#ifdef DIT_NO_NT_LOAD
+constexpr bool kNtLn = false, kNtRms = false, kNtTanh = false, kNtGate = false;
+#else
+constexpr bool kNtLn = false, kNtRms = false, kNtTanh = true, kNtGate = true;
+#endif
+
 // Register budget: at least W6 waves per SIMD at dim <= 3072 (NC <= 6),
-// scaled down in proportion for longer rows.
+// scaled down in proportion (rounded) for longer rows.
 constexpr int waves_per_simd(int nc, int w6) {
-  return nc <= 6 ? w6 : (w6 * 6 / nc > 1 ? w6 * 6 / nc : 1);
+  return nc <= 6 ? w6 : ((w6 * 6 + nc / 2) / nc > 1 ? (w6 * 6 + nc / 2) / nc : 1);
 }
 #define DIT_OCCUPANCY(NC, W6) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NC, W6), 8)))
 
@@ -46,15 +57,27 @@ __device__ __forceinline__ bool valid(int c, int lane, int dim) {
   return c < NC - 1 || 512 * c + 8 * lane < dim;
 }
 
-template <int NC>
+// One row of NC vectors; STREAM selects the nontemporal policy.
+template <int NC, bool STREAM>
 __device__ __forceinline__ void load_row(V8 (&v)[NC], const uint16_t *base, int lane, int dim) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (valid<NC>(c, lane, dim))
-      v[c] = load8(base + 512 * c + 8 * lane);
+      v[c] = STREAM ? load8_stream(base + 512 * c + 8 * lane) : load8(base + 512 * c + 8 * lane);
     else
       v[c] = V8{{0u, 0u, 0u, 0u}};
   }
+}
+
+// Modulation rows read by one row only (per-token) are streamed; rows shared
+// by a few consecutive rows keep the default policy.
+template <int NC>
+__device__ __forceinline__ void load_mod_row(V8 (&v)[NC], const uint16_t *base, int lane, int dim,
+                                             bool per_token) {
+  if (per_token)
+    load_row<NC, true>(v, base, lane, dim);
+  else
+    load_row<NC, false>(v, base, lane, dim);
 }
 
 // One LDS "row" holds NC * 64 vectors of 8 bf16 (vector index = element / 8).
@@ -106,10 +129,10 @@ __device__ __forceinline__ ModSlots mod_slots(const Span &s, int64_t per_mod) {
 
 // ---------------------------------------------------------------------------
 // LayerNorm + AdaLN modulate
-// LDS (staged): [slot][0] = bf(1 + scale), [slot][1] = shift.
+// LDS (staged): [2 slot] = bf(1 + scale), [2 slot + 1] = shift.
 // ---------------------------------------------------------------------------
 template <int NC, int MODE, bool STAGED>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 4) void k_ln_modulate(LnModArgs a) {
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(LnModArgs a) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   const Span sp = spans(a.rows, a.rows_per_wave);
@@ -133,12 +156,12 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 4) void k_ln_modulate(L
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 xv[NC];
-    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC, kNtLn>(xv, a.x + r * a.x_rs, lane, dim);
     const int64_t m = r / a.per_mod;
     V8 s1[NC], sh[NC];
     if (!STAGED) {
-      load_row<NC>(s1, a.scale + m * a.mod_rs, lane, dim);
-      load_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim);
+      load_mod_row<NC>(s1, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
+      load_mod_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
     }
 
     // pass 1: mean
@@ -148,20 +171,17 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 4) void k_ln_modulate(L
     for (int c = 0; c < NC; ++c)
       if (valid<NC>(c, lane, dim))
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          d[c][j] = elem(xv[c], j);
-          p = p + d[c][j];
-        }
+        for (int j = 0; j < 8; ++j) p = p + elem(xv[c], j);
     const float mean = wave_sum(p) / (float)dim;
 
-    // pass 2: deviations and their squares
+    // pass 2: deviations (kept for the output) and their squares
     float q = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       if (valid<NC>(c, lane, dim))
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          d[c][j] = d[c][j] - mean;
+          d[c][j] = elem(xv[c], j) - mean;
           if (MODE == kLossless)
             q = q + d[c][j] * d[c][j];
           else
@@ -234,17 +254,16 @@ __device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, uint32
   round2(y0, y1);
 }
 
-// LDS (staged): [0] = weight, [1 + slot] = scale.
+// LDS: [0] = weight (always), [1 + slot] = scale (staged).
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale(RmsScaleArgs a) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   const Span sp = spans(a.rows, a.rows_per_wave);
   constexpr int kRow = NC * 64;
-  ModSlots ms{0, 0};
-  if (STAGED) {
-    if (sp.wg_first > sp.wg_last) return;
-    ms = mod_slots(sp, a.per_mod);
+  if (sp.wg_first > sp.wg_last) return;                    // whole workgroup idle
+  const ModSlots ms = STAGED ? mod_slots(sp, a.per_mod) : ModSlots{0, 0};
+  {
     const int nv = dim / 8;
     for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
       const int t = i / nv, v = i - t * nv;
@@ -256,17 +275,12 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 xv[NC], wv[NC], sc[NC];
-    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
     const int64_t m = r / a.per_mod;
-    if (!STAGED) {
-      load_row<NC>(wv, a.weight, lane, dim);
-      load_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim);
-    }
+    if (!STAGED) load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    if (STAGED) {
-      lds_row<NC>(wv, lds, lane, dim);
-      lds_row<NC>(sc, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
-    }
+    lds_row<NC>(wv, lds, lane, dim);
+    if (STAGED) lds_row<NC>(sc, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -283,18 +297,17 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale
   }
 }
 
-// LDS (staged): [0] = weight, [1 + slot] = tanh(gate).
+// LDS: [0] = weight (always), [1 + slot] = tanh(gate) (staged).
 template <int NC, int MODE, bool STAGED>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_rmsnorm_tanh_residual(
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_residual(
     RmsTanhArgs a) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   const Span sp = spans(a.rows, a.rows_per_wave);
   constexpr int kRow = NC * 64;
-  ModSlots ms{0, 0};
-  if (STAGED) {
-    if (sp.wg_first > sp.wg_last) return;
-    ms = mod_slots(sp, a.per_mod);
+  if (sp.wg_first > sp.wg_last) return;                    // whole workgroup idle
+  const ModSlots ms = STAGED ? mod_slots(sp, a.per_mod) : ModSlots{0, 0};
+  {
     const int nv = dim / 8;
     for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
       const int t = i / nv, v = i - t * nv;
@@ -302,9 +315,10 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
         lds_put(lds, v, load8(a.weight + 8 * v));
       } else {
         V8 g = load8(a.gate + (ms.m0 + t - 1) * a.mod_rs + 8 * v);
+        float tg[8];
+        tanh8<MODE>(tg, g);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          g.w[k] = pack(tanh_bf16<MODE>(lo(g.w[k])), tanh_bf16<MODE>(hi(g.w[k])));
+        for (int k = 0; k < 4; ++k) g.w[k] = pack(tg[2 * k], tg[2 * k + 1]);
         lds_put(lds + t * kRow, v, g);
       }
     }
@@ -313,36 +327,30 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 xv[NC], rv[NC], wv[NC], tau[NC];
-    load_row<NC>(xv, a.x + r * a.x_rs, lane, dim);
-    load_row<NC>(rv, a.residual + r * a.res_rs, lane, dim);
+    load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
     const int64_t m = r / a.per_mod;
-    if (!STAGED) {
-      load_row<NC>(wv, a.weight, lane, dim);
-      load_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim);
-    }
+    if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    if (STAGED) {
-      lds_row<NC>(wv, lds, lane, dim);
-      lds_row<NC>(tau, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
-    }
+    lds_row<NC>(wv, lds, lane, dim);
+    if (STAGED) lds_row<NC>(tau, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!valid<NC>(c, lane, dim)) continue;
+      float tg[8];
+      if (STAGED) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tg[j] = elem(tau[c], j);
+      } else {
+        tanh8<MODE>(tg, tau[c]);
+      }
       V8 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float y0, y1;
         rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
-        float t0, t1;
-        if (STAGED) {
-          t0 = lo(tau[c].w[k]);
-          t1 = hi(tau[c].w[k]);
-        } else {
-          t0 = tanh_bf16<MODE>(lo(tau[c].w[k]));
-          t1 = tanh_bf16<MODE>(hi(tau[c].w[k]));
-        }
-        float q0 = t0 * y0, q1 = t1 * y1;
+        float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
         round2(q0, q1);                                   // bf(tanh(gate) * y2)
         o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
       }
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
 // LDS (staged): [slot] = gate.
 // ---------------------------------------------------------------------------
 template <int NC, bool STAGED>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 5) void k_residual_gate_add(
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_residual_gate_add(
     GateAddArgs a) {
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
@@ -376,13 +384,13 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 5) void k_residual_gate
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 rv[NC], yv[NC], gv[NC];
-    load_row<NC>(rv, a.residual + r * a.res_rs, lane, dim);
-    load_row<NC>(yv, a.y + r * a.y_rs, lane, dim);
+    load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
+    load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
     const int64_t m = r / a.per_mod;
     if (STAGED)
       lds_row<NC>(gv, lds + (int)(m - ms.m0) * kRow, lane, dim);
     else
-      load_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim);
+      load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -402,13 +410,13 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 5) void k_residual_gate
 
 // ---------------------------------------------------------------------------
 // Launch shape.
-//   Staged (per-batch) modulation: a run of rows per wave, aiming at about
-//   kTargetWaves waves in flight (MI355X: 256 CUs x 4 SIMDs x 4), and only
-//   when every workgroup's 4 * rows_per_wave rows meet at most two
-//   modulation rows.
-//   Otherwise (per-token modulation): one row per wave.
+//   Each wave gets a run of up to max_run rows, aiming at about kTargetWaves
+//   waves (MI355X: 256 CUs x 4 SIMDs x 4).  Modulation is staged in LDS when
+//   every workgroup's 4 * rows_per_wave rows meet at most two modulation
+//   rows (per-batch modulation); otherwise each wave loads it (per-token).
 // ---------------------------------------------------------------------------
 constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kMaxRun = 4;
 
 struct Shape {
   int64_t rows_per_wave;
@@ -416,20 +424,20 @@ struct Shape {
   dim3 grid;
 };
 
-static Shape row_shape(int64_t rows, int64_t per_mod) {
+// max_run: 1 for the kernels whose per-row work is cheap (measured fastest
+// with one row per wave); kMaxRun where staged per-batch work (tanh) is
+// worth sharing across more rows.
+static Shape row_shape(int64_t rows, int64_t per_mod, int64_t max_run) {
   Shape s;
   s.rows_per_wave = (rows + kTargetWaves - 1) / kTargetWaves;
+  if (s.rows_per_wave > max_run) s.rows_per_wave = max_run;
 #ifdef DIT_TUNING
   if (const char *e = getenv("DIT_ROWS_PER_WAVE")) s.rows_per_wave = atoll(e);
 #endif
   if (s.rows_per_wave < 1) s.rows_per_wave = 1;
   s.staged = per_mod >= kWavesPerBlock * s.rows_per_wave;
-  if (!s.staged) s.rows_per_wave = 1;
 #ifdef DIT_TUNING
-  if (getenv("DIT_NO_STAGING")) {
-    s.staged = false;
-    s.rows_per_wave = 1;
-  }
+  if (getenv("DIT_NO_STAGING")) s.staged = false;
 #endif
   const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
   s.grid = dim3((unsigned)((rows + wg_rows - 1) / wg_rows));
@@ -456,7 +464,7 @@ static size_t lds_bytes(int64_t dim, int rows) {
 
 template <int MODE>
 static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1);
   a.rows_per_wave = sh.rows_per_wave;
   const size_t shm = sh.staged ? lds_bytes(a.dim, 4) : 0;
 #define X(N)                                                                          \
@@ -472,15 +480,15 @@ static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = sh.staged ? lds_bytes(a.dim, 3) : 0;
+  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1);
 #define X(N)                                                                            \
   case N:                                                                               \
     if (sh.staged)                                                                      \
       DIT_LAUNCH((k_rmsnorm_scale<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
     else                                                                                \
-      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a);  \
+      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, false>), sh.grid, dim3(kThreads), shm, s, a); \
     break;
   DIT_ROW_DISPATCH();
 #undef X
@@ -488,16 +496,16 @@ static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod);
+  const Shape sh = row_shape(a.rows, a.per_mod, kMaxRun);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = sh.staged ? lds_bytes(a.dim, 3) : 0;
+  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1);
 #define X(N)                                                                                  \
   case N:                                                                                     \
     if (sh.staged)                                                                            \
       DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, \
                  a);                                                                          \
     else                                                                                      \
-      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, false>), sh.grid, dim3(kThreads), 0, s,  \
+      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, false>), sh.grid, dim3(kThreads), shm, s, \
                  a);                                                                          \
     break;
   DIT_ROW_DISPATCH();
@@ -505,7 +513,7 @@ static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
 }
 
 static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1);
   a.rows_per_wave = sh.rows_per_wave;
   const size_t shm = sh.staged ? lds_bytes(a.dim, 2) : 0;
 #define X(N)                                                                              \

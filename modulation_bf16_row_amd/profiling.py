@@ -1,0 +1,143 @@
+"""Text summaries of rocprofv3 result databases (SQLite, rocpd schema).
+
+  python -m modulation_bf16_row_amd.profiling trace RESULTS.db OUT.txt --command "..."
+      per-kernel dispatch statistics from a --kernel-trace run
+  python -m modulation_bf16_row_amd.profiling traffic FETCH.db WRITE.db OUT.txt \
+        --kernel k_ln_modulate --calib k_probe_copy --calib-bytes 1073741824 --command "..."
+      HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE runs,
+      each scaled by what the same counter reads for a copy dispatch of known
+      size (calib-bytes read and calib-bytes written)
+
+The traffic summary records a hash of the kernel sources; the benchmark only
+reports it while the sources still match.
+"""
+import argparse
+import hashlib
+import os
+import re
+import sqlite3
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources and headers the kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name):
+    return re.sub(r"\(.*$", "", name).strip()
+
+
+def kernel_stats(db):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels").fetchall()
+    by = {}
+    for name, dur in rows:
+        by.setdefault(_short(name), []).append(dur / 1000.0)
+    out = []
+    for name, d in by.items():
+        out.append((name, len(d), statistics.mean(d), statistics.median(d), min(d), max(d),
+                    sum(d)))
+    return sorted(out, key=lambda r: -r[6])
+
+
+def counter_values(db, counter):
+    """kernel name -> list of per-dispatch values of one counter."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, value from counters_collection where "
+                       "counter_name = ?", (counter,)).fetchall()
+    by = {}
+    for name, v in rows:
+        by.setdefault(_short(name), []).append(float(v))
+    return by
+
+
+def _match(by, pattern):
+    keys = [k for k in by if re.search(pattern, k)]
+    if not keys:
+        raise SystemExit(f"no dispatch of {pattern!r} in {sorted(by)}")
+    vals = [v for k in keys for v in by[k]]
+    return statistics.mean(vals), len(vals)
+
+
+def write_trace(db, out, command):
+    lines = [f"# rocprofv3 kernel-trace summary", f"# command: {command}",
+             f"# kernel_source_hash = {kernel_source_hash()}",
+             f"{'kernel':32s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} "
+             f"{'min_us':>10s} {'max_us':>10s} {'total_us':>12s}"]
+    for name, n, avg, med, lo, hi, tot in kernel_stats(db):
+        lines.append(f"{name[:32]:32s} {n:6d} {avg:10.3f} {med:10.3f} {lo:10.3f} {hi:10.3f} "
+                     f"{tot:12.1f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command):
+    fetch = counter_values(fetch_db, "FETCH_SIZE")
+    write = counter_values(write_db, "WRITE_SIZE")
+    f_k, nf = _match(fetch, kernel)
+    w_k, nw = _match(write, kernel)
+    f_c, _ = _match(fetch, calib)
+    w_c, _ = _match(write, calib)
+    f_scale = calib_bytes / (f_c * 1024.0)
+    w_scale = calib_bytes / (w_c * 1024.0)
+    read_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    lines = [
+        "# HBM traffic per dispatch from rocprofv3 memory counters",
+        f"# command: {command}",
+        f"# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by "
+        f"calib_bytes / (counter of the copy dispatch)",
+        f"kernel = {kernel}",
+        f"dispatches_fetch = {nf}",
+        f"dispatches_write = {nw}",
+        f"fetch_kib_per_dispatch = {f_k:.1f}",
+        f"write_kib_per_dispatch = {w_k:.1f}",
+        f"calib_kernel = {calib}",
+        f"calib_bytes_each_way = {calib_bytes}",
+        f"calib_fetch_kib = {f_c:.1f}",
+        f"calib_write_kib = {w_c:.1f}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"hbm_read_bytes_per_launch = {read_b:.0f}",
+        f"hbm_write_bytes_per_launch = {write_b:.0f}",
+        f"hbm_bytes_per_launch = {read_b + write_b:.0f}",
+        f"kernel_source_hash = {kernel_source_hash()}",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("out")
+    t.add_argument("--command", default="")
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_db")
+    c.add_argument("write_db")
+    c.add_argument("out")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--calib", default="k_probe_copy")
+    c.add_argument("--calib-bytes", type=float, default=float(1 << 30))
+    c.add_argument("--command", default="")
+    a = ap.parse_args()
+    if a.cmd == "trace":
+        write_trace(a.db, a.out, a.command)
+    else:
+        write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command)
+
+
+if __name__ == "__main__":
+    main()
