@@ -46,8 +46,8 @@
  *   bf16 (nearest even) exactly where the eager PyTorch chain rounds; row
  *   sums use the order R(D) below.  The output is bit-for-bit deterministic.
  *   DIT_MODE_FAST: hardware reciprocal square root, fused multiply-add inside
- *   the sums and the RoPE products, and a plain binary32 tanh; every bf16
- *   rounding point of the lossless chain is kept.  The hardware rsqrt reads a
+ *   the sums and the RoPE products; every bf16 rounding point of the
+ *   lossless chain is kept, and tanh(gate) is the same exact table value.  The hardware rsqrt reads a
  *   subnormal argument as zero (result +inf); the norms only reach that with
  *   eps < 2^-126.
  * Reduction order R(D) (D <= 8192, D % 8 == 0).  A 64-lane wave holds one
@@ -148,8 +148,9 @@ dit_status_t dit_rmsnorm_scale(void *out, int64_t out_rs, const void *x, int64_t
  *   tau = T(gate[m])  -- the correctly rounded bf16 of tanh of the bf16 gate
  *   out = bf( residual + bf(tau * y2) )
  * residual: [rows, dim], row stride res_rs.  gate: [mod_rows, dim].
- * FAST mode: rsqrt as above and tau from a plain binary32 tanh (within one
- * bf16 step of the correctly rounded value).
+ * tau is taken from a 736-entry table of correctly rounded values (built per
+ * workgroup in LDS) for 2^-4 <= |gate| < 3.5; tau = gate below that range and
+ * +-1 above it, both exact.  FAST mode differs only in the rsqrt (as above).
  */
 dit_status_t dit_rmsnorm_tanh_residual(void *out, int64_t out_rs, const void *x, int64_t x_rs,
                                        const void *residual, int64_t res_rs, const void *weight,

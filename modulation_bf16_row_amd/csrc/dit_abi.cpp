@@ -372,7 +372,8 @@ dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hip
 
 dit_status_t dit_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
                              hipStream_t stream) {
-  if (op < DIT_PROBE_ONE_PLUS || op > DIT_PROBE_RMS_RSTD) return fail(DIT_ERR_INVALID, "bad op");
+  if (op < DIT_PROBE_ONE_PLUS || op > DIT_PROBE_TANH_TABLE)
+    return fail(DIT_ERR_INVALID, "bad op");
   if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
     return fail(DIT_ERR_INVALID, "unknown mode");
   if (n < 0) return fail(DIT_ERR_INVALID, "negative size");

@@ -159,17 +159,16 @@ __device__ __forceinline__ float tanh_try(float g, uint32_t &need, int bit) {
   return copysignf(r, g);
 }
 
-// Re-evaluates in binary64 (rounded once) the elements of t flagged in need.
-// One inline copy of the binary64 evaluation serves all N elements: the
-// flagged element is selected, evaluated and written back in a loop.
-template <int N>
-__device__ __forceinline__ void tanh_fix(float (&t)[N], const float (&g)[N], uint32_t need) {
+// Re-evaluates in binary64 (rounded once) the elements of t flagged in need;
+// gate(j) returns gate j.  One inline copy of the binary64 evaluation serves
+// all N elements: the flagged element is fetched, evaluated and written back
+// in a loop.
+template <int N, class Gate>
+__device__ __forceinline__ void tanh_fix(float (&t)[N], uint32_t need, Gate gate) {
   while (need) {
     const int j = __builtin_ctz(need);
     need &= need - 1;
-    float gj = g[0];
-#pragma unroll
-    for (int k = 1; k < N; ++k) gj = (j == k) ? g[k] : gj;
+    const float gj = gate(j);
     const float r = copysignf(round_f64(tanh((double)fabsf(gj))), gj);
 #pragma unroll
     for (int k = 0; k < N; ++k) t[k] = (j == k) ? r : t[k];
@@ -180,11 +179,45 @@ __device__ __forceinline__ void tanh_fix(float (&t)[N], const float (&g)[N], uin
 template <int MODE>
 __device__ __forceinline__ float tanh_bf16(float g) {
   float t[1] = {0.0f};
-  const float gg[1] = {g};
   uint32_t need = 0;
   t[0] = tanh_try<MODE>(g, need, 0);
-  if (MODE == kLossless && need) tanh_fix<1>(t, gg, need);
+  if (MODE == kLossless && need) tanh_fix<1>(t, need, [&](int) { return g; });
   return t[0];
+}
+
+// ---------------------------------------------------------------------------
+// tanh of a bf16 gate by table, as the row kernels use it (both modes).
+//   |g| < 2^-4:   bf(tanh g) = g, since the relative change of tanh, about
+//                 g^2 / 3 < 2^-9.5, is below half a bf16 spacing (>= 2^-9
+//                 relative, also just below a power of two for |g| < 0.076);
+//                 this covers zero and subnormals;
+//   |g| >= 3.5:   +-1, since tanh(3.5) > 1 - 2^-9, the midpoint below 1;
+//                 infinities give +-1, NaN stays NaN (quiet);
+//   otherwise:    one of the 736 magnitudes with bf16 codes 0x3D80..0x405F,
+//                 looked up in a table of their correctly rounded tanh,
+//                 filled from tanh_bf16<kLossless>; the sign is restored.
+// The exhaustive device test checks every one of the 65536 inputs.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kTanhTabLo = 0x3D80u, kTanhTabHi = 0x4060u;
+constexpr int kTanhTabN = (int)(kTanhTabHi - kTanhTabLo);             // 736
+constexpr int kTanhTabVecs = (kTanhTabN * 2 + 15) / 16;               // uint4s
+
+__device__ __forceinline__ void tanh_table_fill(uint16_t *tab, int tid, int nthreads) {
+  for (int i = tid; i < kTanhTabN; i += nthreads) {
+    const float r = tanh_bf16<kLossless>(__uint_as_float((kTanhTabLo + (uint32_t)i) << 16));
+    tab[i] = (uint16_t)(__float_as_uint(r) >> 16);
+  }
+}
+
+// g is a bf16 value (low 16 bits zero).  The table index is clamped, so the
+// LDS access stays inside the table for every input.
+__device__ __forceinline__ float tanh_lookup(float g, const uint16_t *tab) {
+  const uint32_t u = __float_as_uint(g);
+  const uint32_t ab = (u >> 16) & 0x7FFFu, sign = u & 0x80000000u;
+  const uint32_t i = min(ab - kTanhTabLo, (uint32_t)kTanhTabN - 1u);  // wraps when ab < lo
+  const float t = __uint_as_float(((uint32_t)tab[i] << 16) | sign);
+  const float big = ab > 0x7F80u ? g + g : __uint_as_float(0x3F800000u | sign);
+  return ab < kTanhTabLo ? g : (ab >= kTanhTabHi ? big : t);
 }
 
 // 1 / sqrt(v): IEEE square root and division (LOSSLESS) or the hardware
@@ -235,19 +268,6 @@ __device__ __forceinline__ void store8(uint16_t *p, const V8 &v) {
 
 __device__ __forceinline__ float elem(const V8 &v, int j) {
   return (j & 1) ? hi(v.w[j >> 1]) : lo(v.w[j >> 1]);
-}
-
-// tanh of the eight bf16 gates in v, each rounded to bf16 (binary32 values).
-template <int MODE>
-__device__ __forceinline__ void tanh8(float (&t)[8], const V8 &v) {
-  float g[8];
-  uint32_t need = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    g[j] = elem(v, j);
-    t[j] = tanh_try<MODE>(g[j], need, j);
-  }
-  if (MODE == kLossless && need) tanh_fix<8>(t, g, need);
 }
 
 }  // namespace dit

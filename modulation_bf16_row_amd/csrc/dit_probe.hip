@@ -12,9 +12,16 @@ __global__ void k_probe_bf16_round(uint16_t *out, const float *in, int64_t n) {
   if (i < n) out[i] = (uint16_t)(pack(in[i], 0.0f) & 0xFFFFu);
 }
 
-// op 0: bf(1 + s); op 1: tanh to bf16; op 2: bf(1 / sqrt(v)) as in RMSNorm.
+// op 0: bf(1 + s); op 1: tanh to bf16; op 2: bf(1 / sqrt(v)) as in RMSNorm;
+// op 3: tanh through the row kernels' LDS table (filled by each workgroup).
 template <int MODE>
-__global__ void k_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n) {
+__global__ __launch_bounds__(256) void k_probe_unary(int op, uint16_t *out, const uint16_t *in,
+                                                     int64_t n) {
+  __shared__ uint16_t tab[kTanhTabN];
+  if (op == 3) {                                 // op is uniform: every thread reaches the barrier
+    tanh_table_fill(tab, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const float v = __uint_as_float((uint32_t)in[i] << 16);
@@ -23,8 +30,10 @@ __global__ void k_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t
     r = round1(1.0f + v);
   else if (op == 1)
     r = tanh_bf16<MODE>(v);
-  else
+  else if (op == 2)
     r = round1(rsqrt_mode<MODE>(v));
+  else
+    r = tanh_lookup(v, tab);
   out[i] = (uint16_t)(__float_as_uint(r) >> 16);
 }
 

@@ -94,6 +94,12 @@ __device__ __forceinline__ void lds_row(V8 (&v)[NC], const uint4 *row, int lane,
   }
 }
 
+// Chunk c of this lane from one LDS row.
+__device__ __forceinline__ V8 lds_vec(const uint4 *row, int c, int lane) {
+  const uint4 u = row[64 * c + lane];
+  return V8{{u.x, u.y, u.z, u.w}};
+}
+
 __device__ __forceinline__ void lds_put(uint4 *row, int v, const V8 &x) {
   row[v] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
 }
@@ -297,7 +303,8 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale
   }
 }
 
-// LDS: [0] = weight (always), [1 + slot] = tanh(gate) (staged).
+// LDS: [0] = weight (always), [1 + slot] = tanh(gate) (staged), then the
+// tanh table.  tanh comes from the table in both modes.
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_residual(
     RmsTanhArgs a) {
@@ -305,51 +312,54 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   const Span sp = spans(a.rows, a.rows_per_wave);
   constexpr int kRow = NC * 64;
+  uint16_t *tab = reinterpret_cast<uint16_t *>(lds + (STAGED ? 3 : 1) * kRow);
   if (sp.wg_first > sp.wg_last) return;                    // whole workgroup idle
   const ModSlots ms = STAGED ? mod_slots(sp, a.per_mod) : ModSlots{0, 0};
   {
     const int nv = dim / 8;
-    for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
-      const int t = i / nv, v = i - t * nv;
-      if (t == 0) {
-        lds_put(lds, v, load8(a.weight + 8 * v));
-      } else {
-        V8 g = load8(a.gate + (ms.m0 + t - 1) * a.mod_rs + 8 * v);
-        float tg[8];
-        tanh8<MODE>(tg, g);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) g.w[k] = pack(tg[2 * k], tg[2 * k + 1]);
-        lds_put(lds + t * kRow, v, g);
-      }
-    }
+    tanh_table_fill(tab, threadIdx.x, kThreads);
+    for (int v = threadIdx.x; v < nv; v += kThreads) lds_put(lds, v, load8(a.weight + 8 * v));
     __syncthreads();
+    if (STAGED) {
+      for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
+        const int t = i / nv, v = i - t * nv;
+        V8 g = load8(a.gate + (ms.m0 + t) * a.mod_rs + 8 * v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          g.w[k] = pack(tanh_lookup(lo(g.w[k]), tab), tanh_lookup(hi(g.w[k]), tab));
+        lds_put(lds + (1 + t) * kRow, v, g);
+      }
+      __syncthreads();
+    }
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], rv[NC], wv[NC], tau[NC];
+    V8 xv[NC], rv[NC], tau[NC];
     load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
     load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
     const int64_t m = r / a.per_mod;
     if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    lds_row<NC>(wv, lds, lane, dim);
-    if (STAGED) lds_row<NC>(tau, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
+    const uint4 *trow = STAGED ? lds + (1 + (int)(m - ms.m0)) * kRow : lds;
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!valid<NC>(c, lane, dim)) continue;
+      const V8 wc = lds_vec(lds, c, lane);
       float tg[8];
       if (STAGED) {
+        const V8 tc = lds_vec(trow, c, lane);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tg[j] = elem(tau[c], j);
+        for (int j = 0; j < 8; ++j) tg[j] = elem(tc, j);
       } else {
-        tanh8<MODE>(tg, tau[c]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tg[j] = tanh_lookup(elem(tau[c], j), tab);
       }
       V8 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float y0, y1;
-        rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
+        rms_y2(y0, y1, xv[c].w[k], wc.w[k], rstd);
         float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
         round2(q0, q1);                                   // bf(tanh(gate) * y2)
         o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
@@ -498,7 +508,7 @@ template <int MODE>
 static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
   const Shape sh = row_shape(a.rows, a.per_mod, kMaxRun);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1);
+  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1) + kTanhTabVecs * sizeof(uint4);
 #define X(N)                                                                                  \
   case N:                                                                                     \
     if (sh.staged)                                                                            \

@@ -72,6 +72,21 @@ def test_row_ops_shapes(dim, rows, mod_rows):
     _run_all_ops(_inputs(10 * dim + rows, rows, dim, mod_rows), f"dim={dim} rows={rows}/{mod_rows}")
 
 
+@pytest.mark.parametrize("rows,mod_rows,dim,path", [(128, 128, 512, "per-token"),
+                                                    (64, 8, 8192, "staged")])
+def test_tanh_residual_every_gate_code(rows, mod_rows, dim, path):
+    """All 65536 bf16 codes as gates (NaN and infinities included), through
+    the per-token path and through the staged per-batch path."""
+    say("tanh every gate code", path)
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    gate = np.random.default_rng(77).permutation(codes).reshape(mod_rows, dim)
+    x = synth.normal_bf16((rows, dim), 1.0, 7001)
+    res = synth.normal_bf16((rows, dim), 1.0, 7002)
+    w = synth.uniform_bf16((dim,), 0.5, 1.5, 7003)
+    got = host(dit().dit_rmsnorm_tanh_residual(dev(x), dev(res), dev(w), dev(gate), EPS))
+    assert_bits_equal(got, oracle.rmsnorm_tanh_residual(x, res, w, gate, EPS), path)
+
+
 def test_small_adaln_workload():
     """[1, 256, 1024] LN + AdaLN modulate (per-batch scale/shift), then the
     residual gate-add on its output."""

@@ -50,13 +50,23 @@ def test_bf16_round_all_binary32():
         del bits, f
 
 
-@pytest.mark.parametrize("op,name", [(0, "one_plus"), (1, "tanh"), (2, "rms_rstd")])
+@pytest.mark.parametrize("op,name", [(0, "one_plus"), (1, "tanh"), (2, "rms_rstd"),
+                                     (3, "tanh_table")])
 def test_unary_exhaustive_lossless(op, name):
     say("unary", name)
     h = torch.from_numpy(ALL16.view(np.int16)).cuda()
     got = m().dit_probe_unary(op, h, "lossless").cpu().numpy().view(np.uint16)
-    ref = {0: oracle.one_plus, 1: oracle.tanh_bf16, 2: oracle.rms_rstd}[op](ALL16)
+    ref = {0: oracle.one_plus, 1: oracle.tanh_bf16, 2: oracle.rms_rstd,
+           3: oracle.tanh_bf16}[op](ALL16)
     assert_bits_equal(got, ref, name)
+
+
+def test_tanh_table_is_mode_independent():
+    """The row kernels take tanh(gate) from the table in both modes."""
+    say("unary fast tanh_table")
+    h = torch.from_numpy(ALL16.view(np.int16)).cuda()
+    got = m().dit_probe_unary(3, h, "fast").cpu().numpy().view(np.uint16)
+    assert_bits_equal(got, oracle.tanh_bf16(ALL16), "tanh_table fast")
 
 
 @pytest.mark.parametrize("op,name", [(1, "tanh"), (2, "rms_rstd")])
