@@ -20,10 +20,14 @@ value = algorithmic bytes of one step / time per step (GB/s, whole job).  The
 timed steps replay one HIP graph per buffer set (captured from the same five
 calls), so host launch cost does not leave the GPU idle between kernels.
 The roofline object reports LN + AdaLN modulate, the kernel the metric
-names; per-kernel durations come from K further steps launched eagerly from
-prepared calls, each dispatch recording its own start/stop events.
-The CPU baseline runs the oracle (plain C, one thread) over one full step on
-the host and also compares its outputs with the GPU's, bit for bit.
+names; per-kernel durations (mean, median, p10, p90) come from further steps
+launched eagerly from prepared calls, each dispatch recording its own
+start/stop events, in blocks that interleave the two modes (main, other,
+other, main); the other mode's figures are reported beside them.
+The CPU baseline runs the oracle (plain C) over one full step on the host,
+single-threaded (the reported value) and on all threads of the process's
+CPU share (row blocks in parallel), and compares the GPU's outputs with it
+bit for bit.
 """
 import argparse
 import json
@@ -149,48 +153,116 @@ def make_plans(m, s, mode):
     }
 
 
-def cpu_baseline(blk, qkv, gpu_out):
-    """The oracle over one full step on the host (single thread), timed, and
-    its outputs compared with the GPU's bit for bit."""
+def _row_blocks(rows, mod_rows, n):
+    """About n row blocks [a, b), each inside one modulation row."""
+    per_mod = rows // mod_rows
+    k = max(1, -(-n // mod_rows))
+    step = -(-per_mod // k)
+    return [(a, min(a + step, m0 + per_mod), m0 // per_mod)
+            for m0 in range(0, rows, per_mod) for a in range(m0, m0 + per_mod, step)]
+
+
+def oracle_step(blk, qkv, threads):
+    """The oracle over one full step: outputs and seconds per epilogue.  With
+    threads > 1, independent row blocks (and batch x head blocks of the QKV
+    epilogue) are handed to a thread pool; each oracle call is one C call
+    that releases the GIL, and the blocks partition the outputs, so the
+    result is the single-threaded one by construction (and is checked)."""
     import oracle
-    t_ops = {}
-    refs = {}
-    t0 = time.perf_counter()
-    refs["ln_modulate"] = oracle.ln_modulate(blk["x"], blk["scale"], blk["shift"], EPS)
-    t_ops["ln_modulate"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    refs["rmsnorm_scale"] = oracle.rmsnorm_scale(blk["x"], blk["weight"], blk["scale2"], EPS)
-    t_ops["rmsnorm_scale"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    refs["rmsnorm_tanh_residual"] = oracle.rmsnorm_tanh_residual(
-        blk["x"], blk["residual"], blk["weight"], blk["gate"], EPS)
-    t_ops["rmsnorm_tanh_residual"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    refs["residual_gate_add"] = oracle.residual_gate_add(blk["residual"], blk["y"], blk["gate"])
-    t_ops["residual_gate_add"] = time.perf_counter() - t0
+    from concurrent.futures import ThreadPoolExecutor
+    pool = ThreadPoolExecutor(threads) if threads > 1 else None
+
+    def run(fn, jobs):
+        return list(pool.map(fn, jobs)) if pool else [fn(j) for j in jobs]
+
+    x, res, y, w = blk["x"], blk["residual"], blk["y"], blk["weight"]
+    mods = {"ln_modulate": (blk["scale"],), "rmsnorm_scale": (blk["scale2"],),
+            "rmsnorm_tanh_residual": (blk["gate"],), "residual_gate_add": (blk["gate"],)}
+    ops = {
+        "ln_modulate": lambda a, b, m: oracle.ln_modulate(
+            x[a:b], blk["scale"][m:m + 1], blk["shift"][m:m + 1], EPS),
+        "rmsnorm_scale": lambda a, b, m: oracle.rmsnorm_scale(
+            x[a:b], w, blk["scale2"][m:m + 1], EPS),
+        "rmsnorm_tanh_residual": lambda a, b, m: oracle.rmsnorm_tanh_residual(
+            x[a:b], res[a:b], w, blk["gate"][m:m + 1], EPS),
+        "residual_gate_add": lambda a, b, m: oracle.residual_gate_add(
+            res[a:b], y[a:b], blk["gate"][m:m + 1]),
+    }
+    outs, secs = {}, {}
+    for k in ROW_KERNELS:
+        blocks = _row_blocks(ROWS, mods[k][0].shape[0], threads)
+        t0 = time.perf_counter()
+        parts = run(lambda j, f=ops[k]: f(*j), blocks)
+        secs[k] = time.perf_counter() - t0
+        outs[k] = np.concatenate(parts, axis=0)
 
     def views(a):
         return [a[:, :, i * H * DH:(i + 1) * H * DH].reshape(a.shape[0], a.shape[1], H, DH)
                 for i in range(3)]
     tq, tk, tv = views(qkv["txt_qkv"])
     iq, ik, iv = views(qkv["img_qkv"])
+    hb = max(1, H // max(1, -(-threads // B)))
+    jobs = [(b, h, min(h + hb, H)) for b in range(B) for h in range(0, H, hb)]
+
+    def qkv_job(j):
+        b, h0, h1 = j
+        sl = (slice(b, b + 1), slice(None), slice(h0, h1))
+        return oracle.qk_norm_rope(
+            dict(q=tq[sl], k=tk[sl], v=tv[sl], q_weight=qkv["txt_q_weight"],
+                 k_weight=qkv["txt_k_weight"]),
+            dict(q=iq[sl], k=ik[sl], v=iv[sl], q_weight=qkv["img_q_weight"],
+                 k_weight=qkv["img_k_weight"]),
+            qkv["cos"], qkv["sin"], EPS)
     t0 = time.perf_counter()
-    refs["qk_norm_rope"] = oracle.qk_norm_rope(
-        dict(q=tq, k=tk, v=tv, q_weight=qkv["txt_q_weight"], k_weight=qkv["txt_k_weight"]),
-        dict(q=iq, k=ik, v=iv, q_weight=qkv["img_q_weight"], k_weight=qkv["img_k_weight"]),
-        qkv["cos"], qkv["sin"], EPS)
-    t_ops["qk_norm_rope"] = time.perf_counter() - t0
-    total_t = sum(t_ops.values())
-    exact = {}
-    for k in ROW_KERNELS:
-        exact[k] = bool(np.array_equal(gpu_out[k], refs[k]))
-    exact["qk_norm_rope"] = all(np.array_equal(g, r) for g, r in zip(gpu_out["qk_norm_rope"],
-                                                                     refs["qk_norm_rope"]))
-    value = sum(BYTES.values()) / total_t / 1e9
-    return dict(value=round(value, 4), unit="GB/s", cores=1, kind="oracle",
+    parts = run(qkv_job, jobs)
+    secs["qk_norm_rope"] = time.perf_counter() - t0
+    joint = [np.empty((B, S_TXT + S_IMG, H, DH), dtype=np.uint16) for _ in range(3)]
+    for (b, h0, h1), part in zip(jobs, parts):
+        for i in range(3):
+            joint[i][b:b + 1, :, h0:h1] = part[i]
+    outs["qk_norm_rope"] = joint
+    if pool:
+        pool.shutdown()
+    return outs, secs
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _same(a, b):
+    if isinstance(a, list):
+        return all(np.array_equal(u, v) for u, v in zip(a, b))
+    return bool(np.array_equal(a, b))
+
+
+def cpu_baseline(blk, qkv, gpu_out):
+    """The oracle over one full step on the host: one thread (the reported
+    value) and all threads of this process's CPU share (row blocks in
+    parallel, identical outputs); the GPU's outputs are compared with it bit
+    for bit."""
+    refs, t1 = oracle_step(blk, qkv, 1)
+    threads = max(1, min(16, int(os.environ.get("OMP_NUM_THREADS", "16")),
+                         len(os.sched_getaffinity(0))))
+    refs_n, tn = oracle_step(blk, qkv, threads)
+    assert all(_same(refs[k], refs_n[k]) for k in KERNELS), "threaded oracle differs"
+    exact = {k: _same(gpu_out[k], refs[k]) for k in KERNELS}
+    step_bytes = sum(BYTES.values())
+    s1, sn = sum(t1.values()), sum(tn.values())
+    return dict(value=round(step_bytes / s1 / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample="one full step (all five epilogues at the Qwen-Image 1024x1024 shapes), "
-                       "single-threaded oracle, %.1f s" % total_t,
-                seconds_per_op={k: round(v, 3) for k, v in t_ops.items()}), exact
+                       "single-threaded oracle, %.1f s" % s1,
+                seconds_per_op={k: round(v, 3) for k, v in t1.items()},
+                cpu_model=_cpu_model(),
+                all_threads=dict(value=round(step_bytes / sn / 1e9, 4), unit="GB/s",
+                                 cores=threads, seconds=round(sn, 3))), exact
 
 
 def copy_ceiling(m, torch, nbytes=1 << 30, reps=5):
@@ -266,35 +338,53 @@ def main():
     wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
 
-    # Per-kernel durations: K more steps launched eagerly from prepared calls,
-    # each dispatch recording its own start/stop events.
-    plans = [make_plans(m, s, args.mode) for s in sets]
-    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-              for _ in range(args.steps)] for k in KERNELS}
-    for k in KERNELS:                  # record once so the HIP events exist
-        for pair in ev[k]:
-            for e in pair:
-                e.record()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.steps):
-        p = plans[i % 2]
+    # Per-kernel durations: eager steps from prepared calls, each dispatch
+    # recording its own start/stop events.  Blocks of K/2 steps alternate the
+    # modes as main, other, other, main (LOSSLESS and FAST interleaved).
+    other = "fast" if args.mode == "lossless" else "lossless"
+    plans = {md: [make_plans(m, s, md) for s in sets] for md in (args.mode, other)}
+    half = max(1, args.steps // 2)
+    samples = {md: {k: [] for k in KERNELS} for md in plans}
+    eager_ms = []
+    for md in (args.mode, other, other, args.mode):
+        ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                  for _ in range(half)] for k in KERNELS}
+        for k in KERNELS:              # record once so the HIP events exist
+            for pair in ev[k]:
+                for e in pair:
+                    e.record()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(half):
+            p = plans[md][i % 2]
+            for k in KERNELS:
+                m.dit_time_next_launch(*ev[k][i])
+                p[k]()
+        e1.record()
+        torch.cuda.synchronize()
+        if md == args.mode:
+            eager_ms.append(e0.elapsed_time(e1) / half)
         for k in KERNELS:
-            m.dit_time_next_launch(*ev[k][i])
-            p[k]()
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms_step = e0.elapsed_time(e1) / args.steps
-    k_us = {k: 1000.0 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev[k]]))
-            for k in KERNELS}
+            samples[md][k] += [1000.0 * a.elapsed_time(b) for a, b in ev[k]]
+    eager_ms_step = float(np.mean(eager_ms))
+
+    def stats(k, us_list):
+        us = float(np.mean(us_list))
+        gbs = BYTES[k] / (us * 1e-6) / 1e9
+        units = ROWS if k in ROW_KERNELS else B * (S_TXT + S_IMG)
+        return dict(us=round(us, 2), median_us=round(float(np.median(us_list)), 2),
+                    p10_us=round(float(np.percentile(us_list, 10)), 2),
+                    p90_us=round(float(np.percentile(us_list, 90)), 2),
+                    bytes=BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
+                    **{("rows_per_s" if k in ROW_KERNELS else "tokens_per_s"):
+                       float("%.4g" % (units / (us * 1e-6)))})
+    per_kernel = {k: stats(k, samples[args.mode][k]) for k in KERNELS}
+    per_kernel_other = {k: stats(k, samples[other][k]) for k in KERNELS}
+    k_us = {k: per_kernel[k]["us"] for k in KERNELS}
 
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    per_kernel = {k: dict(us=round(k_us[k], 2), bytes=BYTES[k],
-                          gbs=round(BYTES[k] / (k_us[k] * 1e-6) / 1e9, 1),
-                          frac=round(BYTES[k] / (k_us[k] * 1e-6) / 1e9 / PEAK_GBS, 4))
-                  for k in KERNELS}
     dom = "ln_modulate"
     achieved = per_kernel[dom]["gbs"]
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
@@ -312,6 +402,7 @@ def main():
                     mode=args.mode, step_bytes=step_bytes, launch="hip graph replay",
                     host_wall_ms_per_step=round(1000 * wall / args.steps, 4)),
         roofline=roofline, kernels=per_kernel,
+        **{"kernels_" + other: per_kernel_other},
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
         copy_ceiling_gbs=copy_ceiling(m, torch),

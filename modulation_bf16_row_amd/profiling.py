@@ -32,7 +32,11 @@ def kernel_source_hash():
 
 
 def _short(name):
-    return re.sub(r"\(.*$", "", name).strip()
+    """Kernel name without return type, namespace and parameter list; template
+    arguments are kept (for the row kernels: chunks, mode (0 = lossless,
+    1 = fast), staged)."""
+    name = re.sub(r"\(.*$", "", name).strip()
+    return re.sub(r"^void ", "", name).replace("dit::", "")
 
 
 def kernel_stats(db):
@@ -43,9 +47,11 @@ def kernel_stats(db):
         by.setdefault(_short(name), []).append(dur / 1000.0)
     out = []
     for name, d in by.items():
-        out.append((name, len(d), statistics.mean(d), statistics.median(d), min(d), max(d),
-                    sum(d)))
-    return sorted(out, key=lambda r: -r[6])
+        d = sorted(d)
+        pct = lambda q: d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))]
+        out.append((name, len(d), statistics.mean(d), statistics.median(d), pct(0.1), pct(0.9),
+                    d[0], d[-1], sum(d)))
+    return sorted(out, key=lambda r: -r[-1])
 
 
 def counter_values(db, counter):
@@ -68,13 +74,14 @@ def _match(by, pattern):
 
 
 def write_trace(db, out, command):
-    lines = [f"# rocprofv3 kernel-trace summary", f"# command: {command}",
+    lines = [f"# rocprofv3 kernel-trace summary (durations in microseconds)",
+             f"# command: {command}",
              f"# kernel_source_hash = {kernel_source_hash()}",
-             f"{'kernel':32s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} "
-             f"{'min_us':>10s} {'max_us':>10s} {'total_us':>12s}"]
-    for name, n, avg, med, lo, hi, tot in kernel_stats(db):
-        lines.append(f"{name[:32]:32s} {n:6d} {avg:10.3f} {med:10.3f} {lo:10.3f} {hi:10.3f} "
-                     f"{tot:12.1f}")
+             f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'p10_us':>9s} "
+             f"{'p90_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>11s}"]
+    for name, n, avg, med, p10, p90, lo, hi, tot in kernel_stats(db):
+        lines.append(f"{name[:40]:40s} {n:6d} {avg:9.3f} {med:9.3f} {p10:9.3f} {p90:9.3f} "
+                     f"{lo:9.3f} {hi:9.3f} {tot:11.1f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
