@@ -73,6 +73,10 @@ def load(path=None):
     lib.orc_residual_gate_add.restype = ctypes.c_int
     lib.orc_residual_gate_add.argtypes = [_u16p, _i64, _u16p, _i64, _u16p, _i64, _u16p, _i64,
                                           _i64, _i64, _i64]
+    lib.orc_gate_add_ln_modulate.restype = ctypes.c_int
+    lib.orc_gate_add_ln_modulate.argtypes = [_u16p, _i64, _u16p, _i64, _u16p, _i64, _u16p, _i64,
+                                             _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
+                                             ctypes.c_float]
     lib.orc_qk_norm_rope.restype = ctypes.c_int
     lib.orc_qk_norm_rope.argtypes = [_u16p, _u16p, _u16p, _i64, _i64,
                                      ctypes.POINTER(QkvStream), ctypes.POINTER(QkvStream),
@@ -270,6 +274,26 @@ def residual_gate_add(residual, y, gate):
     _check(load().orc_residual_gate_add(_p16(out), dim, _p16(residual), r_rs, _p16(y), y_rs,
                                         _p16(gate), m_rs, gate.shape[0], rows, dim))
     return out
+
+
+def gate_add_ln_modulate(residual, y, gate, scale, shift, eps=1e-6):
+    """residual, y [rows, D]; gate, scale, shift [mod_rows, D] (one row stride).
+    Returns (r', out): r' = bf(residual + bf(gate * y)) and out = LN + AdaLN
+    modulate of r'."""
+    r_rs, residual = _rows(residual)
+    y_rs, y = _rows(y)
+    rows, dim = residual.shape
+    m_rs, gate = _mod(gate, dim)
+    m_rs2, scale = _mod(scale, dim)
+    m_rs3, shift = _mod(shift, dim)
+    assert m_rs == m_rs2 == m_rs3 and gate.shape == scale.shape == shift.shape
+    out_res = np.empty((rows, dim), dtype=np.uint16)
+    out = np.empty((rows, dim), dtype=np.uint16)
+    _check(load().orc_gate_add_ln_modulate(_p16(out_res), dim, _p16(out), dim, _p16(residual),
+                                           r_rs, _p16(y), y_rs, _p16(gate), _p16(scale),
+                                           _p16(shift), m_rs, gate.shape[0], rows, dim,
+                                           ctypes.c_float(eps)))
+    return out_res, out
 
 
 def _stream(q, k, v, qw, kw):

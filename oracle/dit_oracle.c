@@ -297,6 +297,37 @@ int orc_residual_gate_add(uint16_t *out, int64_t out_rs, const uint16_t *residua
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gated residual + LayerNorm/AdaLN producer                                 */
+/* [P1 将FP8量化融合到前序算子 (gated residual + LayerNorm/AdaLN, BF16 output);   */
+/*  P1 NVFP4的三组优化 (the block's deferred residual update merged into the    */
+/*  next normalization/modulation)]                                           */
+/* ------------------------------------------------------------------------- */
+
+/* Row r: r' = bf(residual + bf(gate * y)) (as orc_residual_gate_add), written
+ * to out_res; then out = LayerNorm + AdaLN modulate of the bf16 row r' (as
+ * orc_ln_modulate).  gate, scale and shift share mod_rs and mod_rows.  r' goes
+ * through a private row, so out_res or out may be the residual or y. */
+int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *out,
+                             int64_t out_rs, const uint16_t *residual, int64_t res_rs,
+                             const uint16_t *y, int64_t y_rs, const uint16_t *gate,
+                             const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
+                             int64_t mod_rows, int64_t rows, int64_t dim, float eps) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  uint16_t *rp = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)dim);
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t m = r / per_mod;
+    orc_residual_gate_add(rp, dim, residual + r * res_rs, res_rs, y + r * y_rs, y_rs,
+                          gate + m * mod_rs, mod_rs, 1, 1, dim);
+    orc_ln_modulate(out + r * out_rs, out_rs, rp, dim, scale + m * mod_rs, shift + m * mod_rs,
+                    mod_rs, 1, 1, dim, eps);
+    for (int64_t i = 0; i < dim; ++i) out_res[r * out_res_rs + i] = rp[i];
+  }
+  free(rp);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Q/K RMSNorm + interleaved RoPE + joint QKV write                          */
 /* [P1 合并QKV投影时的数值问题: the four steps of the epilogue]                 */
 /* ------------------------------------------------------------------------- */

@@ -44,6 +44,11 @@ int orc_rmsnorm_tanh_residual(uint16_t *out, int64_t out_rs, const uint16_t *x, 
 int orc_residual_gate_add(uint16_t *out, int64_t out_rs, const uint16_t *residual,
                           int64_t res_rs, const uint16_t *y, int64_t y_rs, const uint16_t *gate,
                           int64_t mod_rs, int64_t mod_rows, int64_t rows, int64_t dim);
+int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *out,
+                             int64_t out_rs, const uint16_t *residual, int64_t res_rs,
+                             const uint16_t *y, int64_t y_rs, const uint16_t *gate,
+                             const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
+                             int64_t mod_rows, int64_t rows, int64_t dim, float eps);
 
 typedef struct {
   const uint16_t *q, *k, *v;      /* [B, S, H, Dh] views, head stride Dh */

@@ -63,6 +63,18 @@ MUTANTS = {
         "float gy = bfv(orc_bf16_value(g[i]) * orc_bf16_value(y[r * y_rs + i]));",
         "float gy = orc_bf16_value(g[i]) * orc_bf16_value(y[r * y_rs + i]);",
         ["test_residual_gate_add_exact"]),
+    "fused LN reads the residual instead of r'": (
+        "orc_ln_modulate(out + r * out_rs, out_rs, rp, dim,",
+        "orc_ln_modulate(out + r * out_rs, out_rs, residual + r * res_rs, dim,",
+        ["test_gate_add_ln_cancellation_gives_shift", "test_gate_add_ln_vs_exact_and_double"]),
+    "fused gate from modulation row 0": (
+        "gate + m * mod_rs, mod_rs, 1, 1, dim);",
+        "gate, mod_rs, 1, 1, dim);",
+        ["test_gate_add_ln_vs_exact_and_double"]),
+    "fused shift taken from scale": (
+        "scale + m * mod_rs, shift + m * mod_rs,",
+        "scale + m * mod_rs, scale + m * mod_rs,",
+        ["test_gate_add_ln_zero_gate_constant_residual"]),
     "RoPE sign": (
         "o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);",
         "o[2 * i] = orc_bf16_round(a * c[i] + b * z[i]);",

@@ -502,6 +502,94 @@ def test_rmsnorm_tanh_residual_composition():
 
 
 # --------------------------------------------------------------------------------------
+# Gated residual + LayerNorm/AdaLN producer (page "基于Agent的SGLang扩散模型Kernel优化实践",
+# sections "将FP8量化融合到前序算子" and "NVFP4的三组优化")
+# --------------------------------------------------------------------------------------
+
+def _nonzero_shift(shape, seed):
+    shift = synth.normal_bf16(shape, 0.1, seed)
+    shift[shift & 0x7FFF == 0] = 0x3F80
+    return shift
+
+
+def test_gate_add_ln_zero_gate_constant_residual():
+    """gate = +0: bf(gate * y) is a zero, so r' is the residual (a -0 residual
+    meeting +0 becomes +0); a constant residual row then gives out = shift."""
+    D = 520
+    res = synth.constant_bf16((4, D), -3.25)
+    res[1] = synth.constant_bf16((1, D), 1000.0)
+    y = synth.normal_bf16((4, D), 1.0, 90)
+    gate = np.zeros((2, D), dtype=np.uint16)
+    scale = synth.normal_bf16((2, D), 0.1, 91)
+    shift = _nonzero_shift((2, D), 92)
+    rp, out = oracle.gate_add_ln_modulate(res, y, gate, scale, shift)
+    assert np.array_equal(rp, res)
+    assert np.array_equal(out, np.repeat(shift, 2, axis=0))
+    # signed zeros: -0 + (+0) = +0 and -0 + (-0) = -0
+    res0 = np.full((2, D), 0x8000, dtype=np.uint16)
+    y0 = np.where(np.arange(D) % 2 == 0, 0x3F80, 0xBF80).astype(np.uint16)[None].repeat(2, 0)
+    rp0, _ = oracle.gate_add_ln_modulate(res0, y0, gate, scale, shift)
+    assert np.array_equal(rp0[:, 0::2], np.zeros((2, D // 2), dtype=np.uint16))
+    assert np.array_equal(rp0[:, 1::2], np.full((2, D // 2), 0x8000, dtype=np.uint16))
+
+
+def test_gate_add_ln_cancellation_gives_shift():
+    """gate = 1 and y = -residual: bf(1 * -r) = -r exactly and r + (-r) = +0,
+    so r' is a +0 row, a constant row, and out = shift bitwise."""
+    D = 1032
+    res = synth.normal_bf16((6, D), 1.0, 93)
+    y = res ^ np.uint16(0x8000)
+    gate = np.full((3, D), 0x3F80, dtype=np.uint16)
+    scale = synth.normal_bf16((3, D), 0.1, 94)
+    shift = _nonzero_shift((3, D), 95)
+    rp, out = oracle.gate_add_ln_modulate(res, y, gate, scale, shift)
+    assert np.array_equal(rp, np.zeros_like(res))
+    assert np.array_equal(out, np.repeat(shift, 2, axis=0))
+
+
+@pytest.mark.parametrize("D", [8, 520, 3072])
+def test_gate_add_ln_vs_exact_and_double(D):
+    """r' is the exact sum of two exactly rounded terms (float64 is exact
+    here), and with scale = 0, shift = -0 the output is the LayerNorm of r',
+    within 1 ulp of float64 everywhere and equal on >= 99%.  Per-batch
+    modulation: rows 0..rows/2-1 use row 0 of gate/scale/shift."""
+    rng = np.random.default_rng(96 + D)
+    rows = max(4, 8000 // D) * 2
+    res = _rand_bf16(rng, rows * D, 3).reshape(rows, D)
+    y = _rand_bf16(rng, rows * D, 3).reshape(rows, D)
+    gate = _rand_bf16(rng, 2 * D, 2).reshape(2, D)
+    scale = np.zeros((2, D), dtype=np.uint16)
+    shift = np.full((2, D), 0x8000, dtype=np.uint16)
+    rp, out = oracle.gate_add_ln_modulate(res, y, gate, scale, shift)
+    g_full = np.repeat(gate, rows // 2, axis=0)
+    gy = value_of_bf16(nearest_bf16(value_of_bf16(g_full) * value_of_bf16(y)))
+    s = value_of_bf16(res) + gy
+    assert np.all((s - value_of_bf16(res)) == gy)
+    assert np.array_equal(rp, nearest_bf16(s).reshape(rows, D))
+    tot = eq = 0
+    for r in range(rows):
+        ref_v, _ = _ln_double(value_of_bf16(rp[r]), 1e-6)
+        d = ulp_distance(out[r], nearest_bf16(ref_v))
+        assert d.max() <= 1, (D, r)
+        eq += int((d == 0).sum())
+        tot += D
+    assert eq / tot >= 0.99
+
+
+def test_gate_add_ln_per_batch_equals_repeated_per_token():
+    """Row r uses modulation row r // (rows / mod_rows): per-batch tensors give
+    the same result as the same rows repeated per token."""
+    rows, D = 12, 520
+    res = synth.normal_bf16((rows, D), 1.0, 97)
+    y = synth.normal_bf16((rows, D), 1.0, 98)
+    gate, scale, shift = (synth.normal_bf16((3, D), 0.1, 99 + i) for i in range(3))
+    a = oracle.gate_add_ln_modulate(res, y, gate, scale, shift)
+    rep = [np.repeat(t, rows // 3, axis=0) for t in (gate, scale, shift)]
+    b = oracle.gate_add_ln_modulate(res, y, *rep)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------------------------------
 # Q/K RMSNorm + interleaved RoPE + joint write
 # --------------------------------------------------------------------------------------
 
