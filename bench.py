@@ -63,6 +63,12 @@ KERNELS = ["residual_gate_add", "ln_modulate", "qk_norm_rope", "rmsnorm_scale",
            "rmsnorm_tanh_residual"]
 ROW_KERNELS = [k for k in KERNELS if k != "qk_norm_rope"]   # (rows, D) outputs
 
+# Fused producers built on the path, measured beside the step (not part of it).
+PRODUCER_BYTES = {
+    # residual, y, r', out; gate, scale, shift
+    "gate_add_ln_modulate": 4 * ROWS * D * 2 + 3 * B * D * 2,
+}
+
 
 def read_traffic(kernel):
     """HBM bytes per launch from the committed counter summary, or None when
@@ -109,6 +115,9 @@ class BufferSet:
         self.w = to_dev(blk["weight"], torch)
         self.out = {k: torch.empty((ROWS, D), dtype=torch.bfloat16, device="cuda")
                     for k in ROW_KERNELS}
+        # outputs of the fused producers (kept apart from the step's outputs)
+        self.prod = {k: torch.empty((ROWS, D), dtype=torch.bfloat16, device="cuda")
+                     for k in ("residual", "out")}
         img = to_dev(qkv["img_qkv"], torch)
         txt = to_dev(qkv["txt_qkv"], torch)
         self._keep = (img, txt)
@@ -151,6 +160,44 @@ def make_plans(m, s, mode):
         "qk_norm_rope": m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode,
                                            out=s.qkv_out, prepare=True),
     }
+
+
+def time_producers(m, torch, sets, mode, steps):
+    """Each fused producer back to back over the two buffer sets, and the
+    unfused calls it replaces, each dispatch timed by its own events."""
+    def run(calls):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls * steps]
+        for a, b in ev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(steps):
+            for j, c in enumerate(calls):
+                m.dit_time_next_launch(*ev[i * len(calls) + j])
+                c[i % 2]()
+        torch.cuda.synchronize()
+        us = [1000.0 * a.elapsed_time(b) for a, b in ev]
+        return float(np.mean(us)) * len(calls), us
+
+    fused = [m.dit_gate_add_ln_modulate(s.res, s.y, s.gate, s.scale, s.shift, EPS, mode,
+                                        out_residual=s.prod["residual"], out=s.prod["out"],
+                                        prepare=True) for s in sets]
+    gate = [m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.prod["residual"],
+                                    prepare=True) for s in sets]
+    ln = [m.dit_ln_modulate(s.prod["residual"], s.scale, s.shift, EPS, mode,
+                            out=s.prod["out"], prepare=True) for s in sets]
+    run([fused])                                     # warm-up
+    us, samples = run([fused])
+    pair_us, _ = run([gate, ln])
+    k = "gate_add_ln_modulate"
+    gbs = PRODUCER_BYTES[k] / (us * 1e-6) / 1e9
+    return {k: dict(us=round(us, 2), median_us=round(float(np.median(samples)), 2),
+                    p10_us=round(float(np.percentile(samples, 10)), 2),
+                    p90_us=round(float(np.percentile(samples, 90)), 2),
+                    bytes=PRODUCER_BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
+                    rows_per_s=float("%.4g" % (ROWS / (us * 1e-6))),
+                    unfused_pair_us=round(pair_us, 2),
+                    note="back to back; replaces residual_gate_add + ln_modulate")}
 
 
 def _row_blocks(rows, mod_rows, n):
@@ -405,6 +452,7 @@ def main():
         **{"kernels_" + other: per_kernel_other},
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
+        producers=time_producers(m, torch, sets, args.mode, args.steps),
         copy_ceiling_gbs=copy_ceiling(m, torch),
     )
     if not args.no_cpu:

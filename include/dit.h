@@ -87,7 +87,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 1
+#define DIT_ABI_VERSION 2
 #define DIT_MAX_DIM 8192
 #define DIT_QK_HEAD_DIM 128
 

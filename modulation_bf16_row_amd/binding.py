@@ -61,6 +61,8 @@ SIGNATURES = {
                                   _i64, _f32, _int, _vp],
     "dit_residual_gate_add": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int,
                               _vp],
+    "dit_gate_add_ln_modulate": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                                 _i64, _i64, _i64, _f32, _int, _vp],
     "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
                          ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
     "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
@@ -255,6 +257,30 @@ def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None, prepare=
     return _call("dit_residual_gate_add", out, prepare, out.data_ptr(), o_rs, residual.data_ptr(),
                  r_rs, y.data_ptr(), y_rs, gate.data_ptr(), mrs, mrows, rows, dim, _mode(mode),
                  _stream(residual))
+
+
+def dit_gate_add_ln_modulate(residual, y, gate, scale, shift, eps=1e-6, mode="lossless",
+                             out_residual=None, out=None, prepare=False):
+    """r' = bf(residual + bf(gate * y)) and LN(r') * (1 + scale) + shift in one
+    pass.  Returns (r', out); either output may be given (and may be residual
+    or y itself)."""
+    _same_device(residual, y, gate, scale, shift)
+    rows, r_rs = _flat_rows(residual, "residual")
+    dim = residual.shape[-1]
+    if y.shape != residual.shape:
+        raise DitInvalid("y must have the shape of residual")
+    _, y_rs = _flat_rows(y, "y")
+    mrows, mrs = _mod_rows(gate, scale, dim, ("gate", "scale"))
+    _mod_rows(gate, shift, dim, ("gate", "shift"))
+    out_residual = _out_like(residual, out_residual)
+    out = _out_like(residual, out)
+    _same_device(residual, out_residual, out)
+    _, rr_rs = _flat_rows(out_residual, "out_residual")
+    _, o_rs = _flat_rows(out, "out")
+    return _call("dit_gate_add_ln_modulate", (out_residual, out), prepare,
+                 out_residual.data_ptr(), rr_rs, out.data_ptr(), o_rs, residual.data_ptr(), r_rs,
+                 y.data_ptr(), y_rs, gate.data_ptr(), scale.data_ptr(), shift.data_ptr(), mrs,
+                 mrows, rows, dim, eps, _mode(mode), _stream(residual))
 
 
 def _qkv_stream(st):

@@ -16,6 +16,7 @@
 #include "dit.h"
 #include "dit_launch.hpp"
 #include "dit_probe.h"
+#include "dit_producers.h"
 #include "dit_timing.h"
 
 namespace {
@@ -239,6 +240,38 @@ dit_status_t dit_residual_gate_add(void *out, int64_t out_rs, const void *residu
   dit::GateAddArgs a{static_cast<uint16_t *>(out), u16(residual), u16(y), u16(gate), out_rs,
                      res_rs, y_rs, mod_rs, rows, dim, rows / mod_rows};
   return hip_status(dit::launch_residual_gate_add(a, stream));
+}
+
+dit_status_t dit_gate_add_ln_modulate(void *out_residual, int64_t out_res_rs, void *out,
+                                      int64_t out_rs, const void *residual, int64_t res_rs,
+                                      const void *y, int64_t y_rs, const void *gate,
+                                      const void *scale, const void *shift, int64_t mod_rs,
+                                      int64_t mod_rows, int64_t rows, int64_t dim, float eps,
+                                      int mode, hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out_residual, out_res_rs, rows, dim, "out_residual is NULL",
+                     "bad out_residual row stride"));
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(residual, res_rs, rows, dim, "residual is NULL", "bad residual row stride"));
+  DIT_TRY(check_rows(y, y_rs, rows, dim, "y is NULL", "bad y row stride"));
+  DIT_TRY(check_rows(gate, mod_rs, mod_rows, dim, "gate is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(shift, mod_rs, mod_rows, dim, "shift is NULL", "bad modulation row stride"));
+  const Span sr = rows_span(out_residual, out_res_rs, rows, dim);
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(residual, res_rs, rows, dim), rows_span(y, y_rs, rows, dim)};
+  const Span cs[] = {rows_span(gate, mod_rs, mod_rows, dim),
+                     rows_span(scale, mod_rs, mod_rows, dim),
+                     rows_span(shift, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(sr, ins, 2, cs, 3));
+  DIT_TRY(check_out_alias(so, ins, 2, cs, 3));
+  if (spans_overlap(sr, so)) return fail(DIT_ERR_INVALID, "the two outputs overlap");
+  dit::GateLnArgs a{static_cast<uint16_t *>(out_residual), static_cast<uint16_t *>(out),
+                    u16(residual), u16(y), u16(gate), u16(scale), u16(shift), out_res_rs, out_rs,
+                    res_rs, y_rs, mod_rs, rows, dim, rows / mod_rows, eps};
+  return hip_status(dit::launch_gate_add_ln_modulate(a, mode, stream));
 }
 
 }  // extern "C"

@@ -33,6 +33,15 @@ struct LnModArgs {
   int64_t rows_per_wave;       // set by the launcher
 };
 
+struct GateLnArgs {
+  uint16_t *out_res, *out;
+  const uint16_t *residual, *y, *gate, *scale, *shift;
+  int64_t out_res_rs, out_rs, res_rs, y_rs, mod_rs;
+  int64_t rows, dim, per_mod;  // per_mod = rows / mod_rows
+  float eps;
+  int64_t rows_per_wave;       // set by the launcher
+};
+
 struct RmsScaleArgs {
   uint16_t *out;
   const uint16_t *x, *weight, *scale;
@@ -77,6 +86,7 @@ struct QkvArgs {
 };
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s);
+hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t s);
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s);
 hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStream_t s);
 hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t s);

@@ -134,6 +134,70 @@ __device__ __forceinline__ ModSlots mod_slots(const Span &s, int64_t per_mod) {
 }
 
 // ---------------------------------------------------------------------------
+// LayerNorm + AdaLN modulate, as two helpers on a row held by the wave.
+// ---------------------------------------------------------------------------
+// Two-pass statistics in order R: returns rho = 1 / sqrt(var + eps) and
+// leaves the deviations x - mean (binary32) in d.
+template <int NC, int MODE>
+__device__ __forceinline__ float ln_stats(const V8 (&xv)[NC], float (&d)[NC][8], int lane,
+                                          int dim, float eps) {
+  float p = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (valid<NC>(c, lane, dim))
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p = p + elem(xv[c], j);
+  const float mean = wave_sum(p) / (float)dim;
+
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (valid<NC>(c, lane, dim))
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        d[c][j] = elem(xv[c], j) - mean;
+        if (MODE == kLossless)
+          q = q + d[c][j] * d[c][j];
+        else
+          q = fmaf(d[c][j], d[c][j], q);
+      }
+  const float var = wave_sum(q) / (float)dim;
+  return rsqrt_mode<MODE>(var + eps);
+}
+
+// bf(1 + scale) of each element, in place.
+template <int NC>
+__device__ __forceinline__ void one_plus_row(V8 (&s)[NC]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s[c].w[k] = pack(1.0f + lo(s[c].w[k]), 1.0f + hi(s[c].w[k]));
+}
+
+// out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) fetches chunk c's
+// bf(1 + scale) and shift.
+template <int NC, class Mod>
+__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, const float (&d)[NC][8],
+                                                float rho, int lane, int dim, Mod mod) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (!valid<NC>(c, lane, dim)) continue;
+    V8 s1, sh;
+    mod(c, s1, sh);
+    V8 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float n0 = d[c][2 * k] * rho, n1 = d[c][2 * k + 1] * rho;
+      round2(n0, n1);                                           // LayerNorm output
+      float p0 = n0 * lo(s1.w[k]), p1 = n1 * hi(s1.w[k]);
+      round2(p0, p1);                                           // product
+      o.w[k] = pack(p0 + lo(sh.w[k]), p1 + hi(sh.w[k]));        // + shift
+    }
+    store8(orow + 512 * c + 8 * lane, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LayerNorm + AdaLN modulate
 // LDS (staged): [2 slot] = bf(1 + scale), [2 slot + 1] = shift.
 // ---------------------------------------------------------------------------
@@ -169,59 +233,94 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(L
       load_mod_row<NC>(s1, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
       load_mod_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
     }
-
-    // pass 1: mean
     float d[NC][8];
-    float p = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (valid<NC>(c, lane, dim))
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p = p + elem(xv[c], j);
-    const float mean = wave_sum(p) / (float)dim;
-
-    // pass 2: deviations (kept for the output) and their squares
-    float q = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (valid<NC>(c, lane, dim))
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          d[c][j] = elem(xv[c], j) - mean;
-          if (MODE == kLossless)
-            q = q + d[c][j] * d[c][j];
-          else
-            q = fmaf(d[c][j], d[c][j], q);
-        }
-    const float var = wave_sum(q) / (float)dim;
-    const float rho = rsqrt_mode<MODE>(var + a.eps);
-
+    const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
     if (STAGED) {
       const int slot = (int)(m - ms.m0);
       lds_row<NC>(s1, lds + (2 * slot + 0) * kRow, lane, dim);
       lds_row<NC>(sh, lds + (2 * slot + 1) * kRow, lane, dim);
     } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          s1[c].w[k] = pack(1.0f + lo(s1[c].w[k]), 1.0f + hi(s1[c].w[k]));  // 1 + scale
+      one_plus_row<NC>(s1);
     }
+    ln_modulate_out<NC>(a.out + r * a.out_rs, d, rho, lane, dim,
+                        [&](int c, V8 &u, V8 &v) { u = s1[c]; v = sh[c]; });
+  }
+}
 
-    uint16_t *orow = a.out + r * a.out_rs;
+// ---------------------------------------------------------------------------
+// Gated residual + LayerNorm + AdaLN modulate: r' = bf(residual + bf(gate * y))
+// is written to out_res, and LN + modulate of r' to out.  The row is read
+// once; r' never goes back through HBM before the LayerNorm.
+// LDS (staged): [3 slot] = gate, [3 slot + 1] = bf(1 + scale), [3 slot + 2] = shift.
+// ---------------------------------------------------------------------------
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_modulate(
+    GateLnArgs a) {
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  const Span sp = spans(a.rows, a.rows_per_wave);
+  constexpr int kRow = NC * 64;
+  ModSlots ms{0, 0};
+  if (STAGED) {
+    if (sp.wg_first > sp.wg_last) return;                  // whole workgroup idle
+    ms = mod_slots(sp, a.per_mod);
+    const int nv = dim / 8;
+    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
+      const int slot = i / nv, v = i - slot * nv;
+      const int64_t off = (ms.m0 + slot) * a.mod_rs + 8 * v;
+      V8 s = load8(a.scale + off);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!valid<NC>(c, lane, dim)) continue;
-      V8 o;
+      for (int k = 0; k < 4; ++k) s.w[k] = pack(1.0f + lo(s.w[k]), 1.0f + hi(s.w[k]));
+      lds_put(lds + (3 * slot + 0) * kRow, v, load8(a.gate + off));
+      lds_put(lds + (3 * slot + 1) * kRow, v, s);
+      lds_put(lds + (3 * slot + 2) * kRow, v, load8(a.shift + off));
+    }
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    const int64_t m = r / a.per_mod;
+    const int slot = STAGED ? (int)(m - ms.m0) : 0;
+    V8 xv[NC];
+    {
+      V8 rv[NC], yv[NC], gv[NC];
+      load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
+      load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
+      if (STAGED)
+        lds_row<NC>(gv, lds + (3 * slot) * kRow, lane, dim);
+      else
+        load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
+      uint16_t *rrow = a.out_res + r * a.out_res_rs;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float n0 = d[c][2 * k] * rho, n1 = d[c][2 * k + 1] * rho;
-        round2(n0, n1);                                           // LayerNorm output
-        float p0 = n0 * lo(s1[c].w[k]), p1 = n1 * hi(s1[c].w[k]);
-        round2(p0, p1);                                           // product
-        o.w[k] = pack(p0 + lo(sh[c].w[k]), p1 + hi(sh[c].w[k]));  // + shift
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float q0 = lo(gv[c].w[k]) * lo(yv[c].w[k]), q1 = hi(gv[c].w[k]) * hi(yv[c].w[k]);
+          round2(q0, q1);                                       // bf(gate * y)
+          xv[c].w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
+        }
+        if (valid<NC>(c, lane, dim)) store8(rrow + 512 * c + 8 * lane, xv[c]);
       }
-      store8(orow + 512 * c + 8 * lane, o);
+    }
+    float d[NC][8];
+    const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
+    uint16_t *orow = a.out + r * a.out_rs;
+    if (STAGED) {
+      const uint4 *s1row = lds + (3 * slot + 1) * kRow, *shrow = lds + (3 * slot + 2) * kRow;
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, V8 &u, V8 &v) {
+        u = lds_vec(s1row, c, lane);
+        v = lds_vec(shrow, c, lane);
+      });
+    } else {
+      const uint16_t *sc = a.scale + m * a.mod_rs + 8 * lane;
+      const uint16_t *sf = a.shift + m * a.mod_rs + 8 * lane;
+      const bool tok = a.per_mod == 1;
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, V8 &u, V8 &v) {
+        u = tok ? load8_stream(sc + 512 * c) : load8(sc + 512 * c);
+        v = tok ? load8_stream(sf + 512 * c) : load8(sf + 512 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u.w[k] = pack(1.0f + lo(u.w[k]), 1.0f + hi(u.w[k]));
+      });
     }
   }
 }
@@ -488,6 +587,27 @@ static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
 #undef X
 }
 
+// Staging three modulation rows per slot stops paying once it limits the
+// workgroups per CU; above this LDS size the wave loads them itself.
+constexpr size_t kMaxStagedLds = 64 * 1024;
+
+template <int MODE>
+static hipError_t gate_ln_dispatch(GateLnArgs a, hipStream_t s) {
+  Shape sh = row_shape(a.rows, a.per_mod, 1);
+  a.rows_per_wave = sh.rows_per_wave;
+  if (lds_bytes(a.dim, 6) > kMaxStagedLds) sh.staged = false;
+  const size_t shm = sh.staged ? lds_bytes(a.dim, 6) : 0;
+#define X(N)                                                                                 \
+  case N:                                                                                    \
+    if (sh.staged)                                                                           \
+      DIT_LAUNCH((k_gate_add_ln_modulate<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
+    else                                                                                     \
+      DIT_LAUNCH((k_gate_add_ln_modulate<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a); \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
+}
+
 template <int MODE>
 static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
   const Shape sh = row_shape(a.rows, a.per_mod, 1);
@@ -539,6 +659,10 @@ static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s) {
   return mode == kFast ? ln_dispatch<kFast>(a, s) : ln_dispatch<kLossless>(a, s);
+}
+
+hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t s) {
+  return mode == kFast ? gate_ln_dispatch<kFast>(a, s) : gate_ln_dispatch<kLossless>(a, s);
 }
 
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s) {

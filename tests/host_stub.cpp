@@ -29,6 +29,13 @@ hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t) {
+  const int64_t v[] = {a.rows,   a.dim,  a.per_mod, a.out_res_rs, a.out_rs,
+                       a.res_rs, a.y_rs, a.mod_rs};
+  rec("gate_add_ln_modulate", mode, v, 8);
+  return hipSuccess;
+}
+
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t) {
   const int64_t v[] = {a.rows, a.dim, a.per_mod, a.out_rs, a.x_rs, a.mod_rs};
   rec("rmsnorm_scale", mode, v, 6);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     lib.dit_abi_version.restype = cint
-    assert lib.dit_abi_version() == 1
+    assert lib.dit_abi_version() == 2
 
 
 @pytest.fixture(scope="module")
@@ -62,6 +62,8 @@ def stub(tmp_path_factory):
                                               i64, f32, cint, vp]
     lib.dit_residual_gate_add.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, cint,
                                           vp]
+    lib.dit_gate_add_ln_modulate.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64,
+                                             i64, i64, i64, f32, cint, vp]
     return lib
 
 
@@ -157,6 +159,45 @@ def test_other_row_ops(stub):
     assert stub.dit_residual_gate_add(OUT, 512, RES, 512, Y, 512, G, 512, 1, 4, 512, 0,
                                       None) == OK
     assert r.name == "residual_gate_add" and r.vals[:3] == [4, 512, 4]
+
+
+def gate_ln(lib, out_res=OUT, out_res_rs=512, out=A * 10, out_rs=512, res=RES, res_rs=512, y=Y,
+            y_rs=512, g=G, sc=SC, sh=SH, mod_rs=512, mod_rows=2, rows=8, dim=512, mode=0):
+    return lib.dit_gate_add_ln_modulate(out_res, out_res_rs, out, out_rs, res, res_rs, y, y_rs, g,
+                                        sc, sh, mod_rs, mod_rows, rows, dim, 1e-6, mode, None)
+
+
+def test_gate_add_ln_accepts_and_forwards(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert gate_ln(stub, rows=12, mod_rows=3, res_rs=1024, out_rs=2048, mode=1) == OK
+    assert r.calls == n0 + 1 and r.name == "gate_add_ln_modulate"
+    assert r.vals[:8] == [12, 512, 4, 512, 2048, 1024, 512, 512]
+    assert ctypes.c_int.in_dll(stub, "stub_mode").value == 1
+    assert gate_ln(stub, out_res=RES) == OK                     # residual updated in place
+    assert gate_ln(stub, out_res=RES, out=Y) == OK              # both outputs in place
+    assert gate_ln(stub, rows=0, res=0, out=0) == OK
+
+
+@pytest.mark.parametrize("kw,status,why", [
+    (dict(out=OUT), INVALID, "outputs overlap"),                  # the two outputs coincide
+    (dict(out=OUT + 1024, out_rs=512), INVALID, "outputs overlap"),
+    (dict(out_res=RES + 16, out_res_rs=512), INVALID, "overlap"),  # partial overlap of residual
+    (dict(out=SH), INVALID, "overlap"),                           # writes a modulation tensor
+    (dict(out_res=G), INVALID, "overlap"),
+    (dict(g=0), INVALID, "NULL"),
+    (dict(out_res=0), INVALID, "NULL"),
+    (dict(mod_rows=3), UNSUPPORTED, "mod_rows"),
+    (dict(dim=8200), UNSUPPORTED, "8192"),
+    (dict(y_rs=500), UNSUPPORTED, "stride"),
+    (dict(mode=7), INVALID, "mode"),
+])
+def test_gate_add_ln_rejections_touch_nothing(stub, kw, status, why):
+    r = Rec(stub)
+    n0 = r.calls
+    assert gate_ln(stub, **kw) == status
+    assert r.calls == n0, "a rejected call must not launch"
+    assert why.lower() in stub.dit_status_reason().decode().lower()
 
 
 class Stream(ctypes.Structure):
