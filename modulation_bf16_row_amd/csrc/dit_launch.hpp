@@ -31,6 +31,7 @@ struct LnModArgs {
   int64_t rows, dim, per_mod;  // per_mod = rows / mod_rows
   float eps;
   int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct GateLnArgs {
@@ -40,6 +41,7 @@ struct GateLnArgs {
   int64_t rows, dim, per_mod;  // per_mod = rows / mod_rows
   float eps;
   int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct RmsScaleArgs {
@@ -48,7 +50,8 @@ struct RmsScaleArgs {
   int64_t out_rs, x_rs, mod_rs;
   int64_t rows, dim, per_mod;
   float eps;
-  int64_t rows_per_wave;
+  int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct RmsTanhArgs {
@@ -57,7 +60,8 @@ struct RmsTanhArgs {
   int64_t out_rs, x_rs, res_rs, mod_rs;
   int64_t rows, dim, per_mod;
   float eps;
-  int64_t rows_per_wave;
+  int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct GateAddArgs {
@@ -65,7 +69,8 @@ struct GateAddArgs {
   const uint16_t *residual, *y, *gate;
   int64_t out_rs, res_rs, y_rs, mod_rs;
   int64_t rows, dim, per_mod;
-  int64_t rows_per_wave;
+  int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct QkvStreamArgs {

@@ -1,30 +1,36 @@
-// dit_rows.hip -- gfx950 kernels for the four row epilogues.
+// dit_rows.hip -- gfx950 kernels for the row epilogues and the gated
+// residual + LayerNorm/AdaLN producer.
 //
 // Geometry.  One 64-lane wave per row at a time; lane l owns the 8-element
 // vectors at 512c + 8l of chunk c (c < NC = ceil(dim / 512)), each moved
 // with one 128-bit access, so a wave-wide access is 1 KiB contiguous.  A
-// wave walks a contiguous run of `rows_per_wave` rows; a 256-thread
-// workgroup (four waves) covers 4 * rows_per_wave consecutive rows.  The
-// row stays in VGPRs between the LayerNorm passes, so x is read from HBM
-// once; latency is hidden by the other waves resident on the SIMD.  Rows
-// and outputs move with the nontemporal cache policy; shared operands with
-// the default one.
+// wave walks a contiguous run of `rows_per_wave` rows of its workgroup
+// (four waves).  The row stays in VGPRs between the LayerNorm passes, so x
+// is read from HBM once; latency is hidden by the other waves resident on
+// the SIMD.  Outputs move with the nontemporal cache policy, row inputs
+// with the per-kernel policy below, shared operands with the default one.
 //
-// Modulation operands.  With per-batch modulation (a workgroup's rows meet
-// at most two modulation rows), the workgroup computes the per-element
-// operands once into LDS -- bf(1 + scale) and shift, the RMSNorm weight and
-// scale, tanh(gate), or gate -- and every wave reads them with one 128-bit
-// LDS access per vector.  With per-token modulation each row's operands are
-// loaded (and transformed) by the wave that uses them.
+// Modulation operands.  With per-batch modulation the grid is laid out per
+// modulation row: blocks_per_mod workgroups cover the rows of one
+// modulation row, so all rows of a workgroup share it.  The workgroup
+// converts its per-element operands once into LDS as binary32 values --
+// bf(1 + scale) and shift, the RMSNorm weight and scale, tanh(gate), or
+// gate -- and the waves read them with two 128-bit LDS accesses per
+// 8-element vector, with no bf16 unpacking in the row loop (the kernels
+// are close to their vector-ALU budget, so every instruction per element
+// counts).  With per-token modulation rows are laid out consecutively and
+// each row's operands are loaded (and transformed) by the wave using them.
 //
 // Sums follow R(dim): each lane adds its own terms in (chunk, element)
 // order, then a fixed xor butterfly across the 64 lanes.
 //
 // Sources: AdaLN rounding points -- page "基于Agent的SGLang扩散模型Kernel优化实践"
-// (tahou.com), section "数学等价不代表结果完全一致"; native bf16 RMSNorm chain --
-// page "#34085 [diffusion] Clean up kernels and shared fast paths", section
-// "关键源码片段"; rmsnorm+tanh(gate)*x+residual and residual+gate*update --
-// page "AI Agent 驱动的 SGLang Kernel 一等公民", section 0x3 / 3.2.
+// (tahou.com), section "数学等价不代表结果完全一致"; gated residual +
+// LayerNorm/AdaLN producer -- same page, sections "将FP8量化融合到前序算子" and
+// "NVFP4的三组优化"; native bf16 RMSNorm chain -- page "#34085 [diffusion] Clean
+// up kernels and shared fast paths", section "关键源码片段";
+// rmsnorm+tanh(gate)*x+residual and residual+gate*update -- page "AI Agent
+// 驱动的 SGLang Kernel 一等公民", section 0x3 / 3.2.
 #include <stdlib.h>
 
 #include "dit_device.hpp"
@@ -80,61 +86,84 @@ __device__ __forceinline__ void load_mod_row(V8 (&v)[NC], const uint16_t *base, 
     load_row<NC, false>(v, base, lane, dim);
 }
 
-// One LDS "row" holds NC * 64 vectors of 8 bf16 (vector index = element / 8).
-template <int NC>
-__device__ __forceinline__ void lds_row(V8 (&v)[NC], const uint4 *row, int lane, int dim) {
+// Keeps the compiler from moving instructions across this point.  Placed
+// between a row's statistics and its output loop, it stops the output's
+// LDS reads from being hoisted above the reductions, where they would all
+// be live at once (more VGPRs, fewer waves per SIMD).
+__device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ void unpack8(const V8 &v, float (&f)[8]) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (valid<NC>(c, lane, dim)) {
-      const uint4 u = row[64 * c + lane];
-      v[c] = V8{{u.x, u.y, u.z, u.w}};
-    } else {
-      v[c] = V8{{0u, 0u, 0u, 0u}};
-    }
-  }
-}
-
-// Chunk c of this lane from one LDS row.
-__device__ __forceinline__ V8 lds_vec(const uint4 *row, int c, int lane) {
-  const uint4 u = row[64 * c + lane];
-  return V8{{u.x, u.y, u.z, u.w}};
-}
-
-__device__ __forceinline__ void lds_put(uint4 *row, int v, const V8 &x) {
-  row[v] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
-}
-
-// Rows of this workgroup and of this wave.
-struct Span {
-  int64_t wg_first, wg_last;    // inclusive range of the workgroup (may be empty)
-  int64_t begin, end;           // the wave's run [begin, end)
-};
-
-__device__ __forceinline__ Span spans(int64_t rows, int64_t rpw) {
-  Span s;
-  s.wg_first = (int64_t)blockIdx.x * kWavesPerBlock * rpw;
-  const int64_t wg_end = s.wg_first + kWavesPerBlock * rpw;
-  s.wg_last = (wg_end < rows ? wg_end : rows) - 1;
-  s.begin = s.wg_first + (int64_t)(threadIdx.x >> 6) * rpw;
-  s.end = s.begin + rpw < rows ? s.begin + rpw : rows;
-  return s;
-}
-
-// Modulation rows of the workgroup: m0 = first, count = 1 or 2.
-struct ModSlots {
-  int64_t m0;
-  int count;
-};
-
-__device__ __forceinline__ ModSlots mod_slots(const Span &s, int64_t per_mod) {
-  ModSlots ms;
-  ms.m0 = s.wg_first / per_mod;
-  ms.count = (int)(s.wg_last / per_mod - ms.m0) + 1;
-  return ms;
+  for (int j = 0; j < 8; ++j) f[j] = elem(v, j);
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm + AdaLN modulate, as two helpers on a row held by the wave.
+// binary32 staging rows in LDS.  Element 512c + 8l + j of a row is component
+// j % 4 of float4 (2c + j / 4) * 64 + l: a lane reads the 8 values of its
+// chunk c with two ds_read_b128, each covering 64 consecutive float4s across
+// the wave (no bank conflicts).  A staged row takes NC * 128 float4s.
+// ---------------------------------------------------------------------------
+template <int NC>
+constexpr int stage_vecs() {
+  return NC * 128;
+}
+
+// Stores the 8 values of vector v (elements 8v .. 8v + 7).
+__device__ __forceinline__ void stage_put(float4 *row, int v, const float (&f)[8]) {
+  const int c = v >> 6, l = v & 63;
+  row[(2 * c) * 64 + l] = make_float4(f[0], f[1], f[2], f[3]);
+  row[(2 * c + 1) * 64 + l] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+__device__ __forceinline__ void stage_get(const float4 *row, int c, int lane, float (&f)[8]) {
+  const float4 a = row[(2 * c) * 64 + lane], b = row[(2 * c + 1) * 64 + lane];
+  f[0] = a.x;
+  f[1] = a.y;
+  f[2] = a.z;
+  f[3] = a.w;
+  f[4] = b.x;
+  f[5] = b.y;
+  f[6] = b.z;
+  f[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Row runs of this wave.
+// ---------------------------------------------------------------------------
+struct Span {
+  int64_t begin, end;   // the wave's rows [begin, end) (may be empty)
+  int64_t m;            // modulation row of the workgroup (staged layout only)
+  bool wg_empty;        // the whole workgroup has no rows
+};
+
+// Consecutive rows: workgroup b covers rows [4 b rpw, 4 (b + 1) rpw).
+__device__ __forceinline__ Span spans(int64_t rows, int64_t rpw) {
+  Span s;
+  const int64_t wg_first = (int64_t)blockIdx.x * kWavesPerBlock * rpw;
+  s.wg_empty = wg_first >= rows;
+  s.begin = wg_first + (int64_t)(threadIdx.x >> 6) * rpw;
+  s.end = s.begin + rpw < rows ? s.begin + rpw : rows;
+  s.m = 0;
+  return s;
+}
+
+// Per modulation row: workgroup b covers block b % blocks_per_mod of the
+// rows of modulation row b / blocks_per_mod; the last block of a modulation
+// row may be short (its trailing waves then have no rows).
+__device__ __forceinline__ Span mod_spans(int64_t per_mod, int64_t rpw, int64_t blocks_per_mod) {
+  Span s;
+  s.m = (int64_t)blockIdx.x / blocks_per_mod;
+  const int64_t i = (int64_t)blockIdx.x - s.m * blocks_per_mod;
+  const int64_t mod_end = (s.m + 1) * per_mod;
+  const int64_t wg_first = s.m * per_mod + i * kWavesPerBlock * rpw;
+  s.wg_empty = false;                                       // i < blocks_per_mod
+  s.begin = wg_first + (int64_t)(threadIdx.x >> 6) * rpw;
+  s.end = s.begin + rpw < mod_end ? s.begin + rpw : mod_end;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm + AdaLN modulate, as helpers on a row held by the wave.
 // ---------------------------------------------------------------------------
 // Two-pass statistics in order R: returns rho = 1 / sqrt(var + eps) and
 // leaves the deviations x - mean (binary32) in d.
@@ -165,85 +194,85 @@ __device__ __forceinline__ float ln_stats(const V8 (&xv)[NC], float (&d)[NC][8],
   return rsqrt_mode<MODE>(var + eps);
 }
 
-// bf(1 + scale) of each element, in place.
-template <int NC>
-__device__ __forceinline__ void one_plus_row(V8 (&s)[NC]) {
+// bf(1 + scale) of each of the 8 values.
+__device__ __forceinline__ void one_plus8(const V8 &s, float (&f)[8]) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s[c].w[k] = pack(1.0f + lo(s[c].w[k]), 1.0f + hi(s[c].w[k]));
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = 1.0f + lo(s.w[k]);
+    f[2 * k + 1] = 1.0f + hi(s.w[k]);
+    round2(f[2 * k], f[2 * k + 1]);
+  }
 }
 
-// out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) fetches chunk c's
-// bf(1 + scale) and shift.
+// out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) gives chunk c's
+// bf(1 + scale) and shift as binary32 values.
 template <int NC, class Mod>
 __device__ __forceinline__ void ln_modulate_out(uint16_t *orow, const float (&d)[NC][8],
                                                 float rho, int lane, int dim, Mod mod) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (!valid<NC>(c, lane, dim)) continue;
-    V8 s1, sh;
+    float s1[8], sh[8];
     mod(c, s1, sh);
     V8 o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float n0 = d[c][2 * k] * rho, n1 = d[c][2 * k + 1] * rho;
       round2(n0, n1);                                           // LayerNorm output
-      float p0 = n0 * lo(s1.w[k]), p1 = n1 * hi(s1.w[k]);
+      float p0 = n0 * s1[2 * k], p1 = n1 * s1[2 * k + 1];
       round2(p0, p1);                                           // product
-      o.w[k] = pack(p0 + lo(sh.w[k]), p1 + hi(sh.w[k]));        // + shift
+      o.w[k] = pack(p0 + sh[2 * k], p1 + sh[2 * k + 1]);        // + shift
     }
     store8(orow + 512 * c + 8 * lane, o);
   }
 }
 
+
 // ---------------------------------------------------------------------------
 // LayerNorm + AdaLN modulate
-// LDS (staged): [2 slot] = bf(1 + scale), [2 slot + 1] = shift.
+// LDS (staged): [0] = bf(1 + scale), [1] = shift, binary32.
 // ---------------------------------------------------------------------------
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(LnModArgs a) {
-  extern __shared__ uint4 lds[];
+  extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  constexpr int kRow = NC * 64;
-  ModSlots ms{0, 0};
+  constexpr int kRow = stage_vecs<NC>();
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
   if (STAGED) {
-    if (sp.wg_first > sp.wg_last) return;                  // whole workgroup idle
-    ms = mod_slots(sp, a.per_mod);
-    const int nv = dim / 8;
-    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
-      const int slot = i / nv, v = i - slot * nv;
-      const int64_t m = ms.m0 + slot;
-      V8 s = load8(a.scale + m * a.mod_rs + 8 * v);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) s.w[k] = pack(1.0f + lo(s.w[k]), 1.0f + hi(s.w[k]));
-      lds_put(lds + (2 * slot + 0) * kRow, v, s);
-      lds_put(lds + (2 * slot + 1) * kRow, v, load8(a.shift + m * a.mod_rs + 8 * v));
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      float s1[8], sh[8];
+      one_plus8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s1);
+      unpack8(load8(a.shift + sp.m * a.mod_rs + 8 * v), sh);
+      stage_put(lds, v, s1);
+      stage_put(lds + kRow, v, sh);
     }
     __syncthreads();
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC];
+    V8 xv[NC], sc[NC], sf[NC];
     load_row<NC, kNtLn>(xv, a.x + r * a.x_rs, lane, dim);
-    const int64_t m = r / a.per_mod;
-    V8 s1[NC], sh[NC];
     if (!STAGED) {
-      load_mod_row<NC>(s1, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
-      load_mod_row<NC>(sh, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
+      const int64_t m = r / a.per_mod;
+      load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
+      load_mod_row<NC>(sf, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
     }
     float d[NC][8];
     const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
+    uint16_t *orow = a.out + r * a.out_rs;
     if (STAGED) {
-      const int slot = (int)(m - ms.m0);
-      lds_row<NC>(s1, lds + (2 * slot + 0) * kRow, lane, dim);
-      lds_row<NC>(sh, lds + (2 * slot + 1) * kRow, lane, dim);
+      phase_barrier();
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
+        stage_get(lds, c, lane, s1);
+        stage_get(lds + kRow, c, lane, sh);
+      });
     } else {
-      one_plus_row<NC>(s1);
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
+        one_plus8(sc[c], s1);
+        unpack8(sf[c], sh);
+      });
     }
-    ln_modulate_out<NC>(a.out + r * a.out_rs, d, rho, lane, dim,
-                        [&](int c, V8 &u, V8 &v) { u = s1[c]; v = sh[c]; });
   }
 }
 
@@ -251,75 +280,77 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(L
 // Gated residual + LayerNorm + AdaLN modulate: r' = bf(residual + bf(gate * y))
 // is written to out_res, and LN + modulate of r' to out.  The row is read
 // once; r' never goes back through HBM before the LayerNorm.
-// LDS (staged): [3 slot] = gate, [3 slot + 1] = bf(1 + scale), [3 slot + 2] = shift.
+// LDS (staged): [0] = gate, [1] = bf(1 + scale), [2] = shift, binary32.
 // ---------------------------------------------------------------------------
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_modulate(
     GateLnArgs a) {
-  extern __shared__ uint4 lds[];
+  extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  constexpr int kRow = NC * 64;
-  ModSlots ms{0, 0};
+  constexpr int kRow = stage_vecs<NC>();
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
   if (STAGED) {
-    if (sp.wg_first > sp.wg_last) return;                  // whole workgroup idle
-    ms = mod_slots(sp, a.per_mod);
-    const int nv = dim / 8;
-    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
-      const int slot = i / nv, v = i - slot * nv;
-      const int64_t off = (ms.m0 + slot) * a.mod_rs + 8 * v;
-      V8 s = load8(a.scale + off);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) s.w[k] = pack(1.0f + lo(s.w[k]), 1.0f + hi(s.w[k]));
-      lds_put(lds + (3 * slot + 0) * kRow, v, load8(a.gate + off));
-      lds_put(lds + (3 * slot + 1) * kRow, v, s);
-      lds_put(lds + (3 * slot + 2) * kRow, v, load8(a.shift + off));
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      const int64_t off = sp.m * a.mod_rs + 8 * v;
+      float g[8], s1[8], sh[8];
+      unpack8(load8(a.gate + off), g);
+      one_plus8(load8(a.scale + off), s1);
+      unpack8(load8(a.shift + off), sh);
+      stage_put(lds, v, g);
+      stage_put(lds + kRow, v, s1);
+      stage_put(lds + 2 * kRow, v, sh);
     }
     __syncthreads();
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    const int64_t m = r / a.per_mod;
-    const int slot = STAGED ? (int)(m - ms.m0) : 0;
-    V8 xv[NC];
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
+    V8 xv[NC], sc[NC], sf[NC];
     {
       V8 rv[NC], yv[NC], gv[NC];
       load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
       load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
-      if (STAGED)
-        lds_row<NC>(gv, lds + (3 * slot) * kRow, lane, dim);
-      else
+      if (!STAGED) {
         load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
+        load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
+        load_mod_row<NC>(sf, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
+      }
       uint16_t *rrow = a.out_res + r * a.out_res_rs;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        if (!valid<NC>(c, lane, dim)) {
+          xv[c] = V8{{0u, 0u, 0u, 0u}};                         // outside the row
+          continue;
+        }
+        float g[8];
+        if (STAGED)
+          stage_get(lds, c, lane, g);
+        else
+          unpack8(gv[c], g);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float q0 = lo(gv[c].w[k]) * lo(yv[c].w[k]), q1 = hi(gv[c].w[k]) * hi(yv[c].w[k]);
+          float q0 = g[2 * k] * lo(yv[c].w[k]), q1 = g[2 * k + 1] * hi(yv[c].w[k]);
           round2(q0, q1);                                       // bf(gate * y)
           xv[c].w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
         }
-        if (valid<NC>(c, lane, dim)) store8(rrow + 512 * c + 8 * lane, xv[c]);
+        store8(rrow + 512 * c + 8 * lane, xv[c]);
       }
     }
+    if (STAGED) phase_barrier();
     float d[NC][8];
     const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
     uint16_t *orow = a.out + r * a.out_rs;
     if (STAGED) {
-      const uint4 *s1row = lds + (3 * slot + 1) * kRow, *shrow = lds + (3 * slot + 2) * kRow;
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, V8 &u, V8 &v) {
-        u = lds_vec(s1row, c, lane);
-        v = lds_vec(shrow, c, lane);
+      phase_barrier();
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
+        stage_get(lds + kRow, c, lane, s1);
+        stage_get(lds + 2 * kRow, c, lane, sh);
       });
     } else {
-      const uint16_t *sc = a.scale + m * a.mod_rs + 8 * lane;
-      const uint16_t *sf = a.shift + m * a.mod_rs + 8 * lane;
-      const bool tok = a.per_mod == 1;
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, V8 &u, V8 &v) {
-        u = tok ? load8_stream(sc + 512 * c) : load8(sc + 512 * c);
-        v = tok ? load8_stream(sf + 512 * c) : load8(sf + 512 * c);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) u.w[k] = pack(1.0f + lo(u.w[k]), 1.0f + hi(u.w[k]));
+      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
+        one_plus8(sc[c], s1);
+        unpack8(sf[c], sh);
       });
     }
   }
@@ -348,108 +379,116 @@ __device__ __forceinline__ float rms_rstd(const V8 (&xv)[NC], int lane, int dim,
   return round1(rsqrt_mode<MODE>(v));                    // bf16 rstd
 }
 
-// y2 = bf(bf(x * rstd) * w) for the pair in word xw.
-__device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, uint32_t ww,
+// y2 = bf(bf(x * rstd) * w) for the pair in word xw (weights w0, w1).
+__device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, float w0, float w1,
                                        float rstd) {
   y0 = lo(xw) * rstd;
   y1 = hi(xw) * rstd;
   round2(y0, y1);
-  y0 = y0 * lo(ww);
-  y1 = y1 * hi(ww);
+  y0 = y0 * w0;
+  y1 = y1 * w1;
   round2(y0, y1);
 }
 
-// LDS: [0] = weight (always), [1 + slot] = scale (staged).
+// The RMSNorm weight as a staged row (every launch, both layouts).
+__device__ __forceinline__ void stage_weight(float4 *row, const uint16_t *weight, int dim) {
+  for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+    float w[8];
+    unpack8(load8(weight + 8 * v), w);
+    stage_put(row, v, w);
+  }
+}
+
+// LDS: [0] = weight (always), [1] = scale (staged), binary32.
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale(RmsScaleArgs a) {
-  extern __shared__ uint4 lds[];
+  extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  constexpr int kRow = NC * 64;
-  if (sp.wg_first > sp.wg_last) return;                    // whole workgroup idle
-  const ModSlots ms = STAGED ? mod_slots(sp, a.per_mod) : ModSlots{0, 0};
-  {
-    const int nv = dim / 8;
-    for (int i = threadIdx.x; i < (1 + ms.count) * nv; i += kThreads) {
-      const int t = i / nv, v = i - t * nv;
-      const uint16_t *src = t == 0 ? a.weight : a.scale + (ms.m0 + t - 1) * a.mod_rs;
-      lds_put(lds + t * kRow, v, load8(src + 8 * v));
+  constexpr int kRow = stage_vecs<NC>();
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
+  if (sp.wg_empty) return;                                 // whole workgroup idle
+  stage_weight(lds, a.weight, dim);
+  if (STAGED) {
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      float s[8];
+      unpack8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s);
+      stage_put(lds + kRow, v, s);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], wv[NC], sc[NC];
+    V8 xv[NC], sc[NC];
     load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
-    const int64_t m = r / a.per_mod;
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
     if (!STAGED) load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    lds_row<NC>(wv, lds, lane, dim);
-    if (STAGED) lds_row<NC>(sc, lds + (1 + (int)(m - ms.m0)) * kRow, lane, dim);
+    phase_barrier();
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!valid<NC>(c, lane, dim)) continue;
+      float w[8], s[8];
+      stage_get(lds, c, lane, w);
+      if (STAGED)
+        stage_get(lds + kRow, c, lane, s);
+      else
+        unpack8(sc[c], s);
       V8 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float y0, y1;
-        rms_y2(y0, y1, xv[c].w[k], wv[c].w[k], rstd);
-        o.w[k] = pack(y0 * lo(sc[c].w[k]), y1 * hi(sc[c].w[k]));
+        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
+        o.w[k] = pack(y0 * s[2 * k], y1 * s[2 * k + 1]);
       }
       store8(orow + 512 * c + 8 * lane, o);
     }
   }
 }
 
-// LDS: [0] = weight (always), [1 + slot] = tanh(gate) (staged), then the
+// LDS: [0] = weight (always), [1] = tanh(gate) (staged), binary32; then the
 // tanh table.  tanh comes from the table in both modes.
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_residual(
     RmsTanhArgs a) {
-  extern __shared__ uint4 lds[];
+  extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  constexpr int kRow = NC * 64;
-  uint16_t *tab = reinterpret_cast<uint16_t *>(lds + (STAGED ? 3 : 1) * kRow);
-  if (sp.wg_first > sp.wg_last) return;                    // whole workgroup idle
-  const ModSlots ms = STAGED ? mod_slots(sp, a.per_mod) : ModSlots{0, 0};
-  {
-    const int nv = dim / 8;
-    tanh_table_fill(tab, threadIdx.x, kThreads);
-    for (int v = threadIdx.x; v < nv; v += kThreads) lds_put(lds, v, load8(a.weight + 8 * v));
-    __syncthreads();
-    if (STAGED) {
-      for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
-        const int t = i / nv, v = i - t * nv;
-        V8 g = load8(a.gate + (ms.m0 + t) * a.mod_rs + 8 * v);
+  constexpr int kRow = stage_vecs<NC>();
+  uint16_t *tab = reinterpret_cast<uint16_t *>(lds + (STAGED ? 2 : 1) * kRow);
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
+  if (sp.wg_empty) return;                                 // whole workgroup idle
+  tanh_table_fill(tab, threadIdx.x, kThreads);
+  stage_weight(lds, a.weight, dim);
+  __syncthreads();
+  if (STAGED) {
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      const V8 g = load8(a.gate + sp.m * a.mod_rs + 8 * v);
+      float t[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          g.w[k] = pack(tanh_lookup(lo(g.w[k]), tab), tanh_lookup(hi(g.w[k]), tab));
-        lds_put(lds + (1 + t) * kRow, v, g);
-      }
-      __syncthreads();
+      for (int j = 0; j < 8; ++j) t[j] = tanh_lookup(elem(g, j), tab);
+      stage_put(lds + kRow, v, t);
     }
+    __syncthreads();
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 xv[NC], rv[NC], tau[NC];
     load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
     load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
-    const int64_t m = r / a.per_mod;
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
     if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    const uint4 *trow = STAGED ? lds + (1 + (int)(m - ms.m0)) * kRow : lds;
+    phase_barrier();
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!valid<NC>(c, lane, dim)) continue;
-      const V8 wc = lds_vec(lds, c, lane);
-      float tg[8];
+      float w[8], tg[8];
+      stage_get(lds, c, lane, w);
       if (STAGED) {
-        const V8 tc = lds_vec(trow, c, lane);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tg[j] = elem(tc, j);
+        stage_get(lds + kRow, c, lane, tg);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) tg[j] = tanh_lookup(elem(tau[c], j), tab);
@@ -458,7 +497,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float y0, y1;
-        rms_y2(y0, y1, xv[c].w[k], wc.w[k], rstd);
+        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
         float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
         round2(q0, q1);                                   // bf(tanh(gate) * y2)
         o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
@@ -470,23 +509,20 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
 
 // ---------------------------------------------------------------------------
 // Residual gate-add: out = bf(residual + bf(gate * y)).
-// LDS (staged): [slot] = gate.
+// LDS (staged): [0] = gate, binary32.
 // ---------------------------------------------------------------------------
 template <int NC, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_residual_gate_add(
     GateAddArgs a) {
-  extern __shared__ uint4 lds[];
+  extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  constexpr int kRow = NC * 64;
-  ModSlots ms{0, 0};
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
   if (STAGED) {
-    if (sp.wg_first > sp.wg_last) return;
-    ms = mod_slots(sp, a.per_mod);
-    const int nv = dim / 8;
-    for (int i = threadIdx.x; i < ms.count * nv; i += kThreads) {
-      const int t = i / nv, v = i - t * nv;
-      lds_put(lds + t * kRow, v, load8(a.gate + (ms.m0 + t) * a.mod_rs + 8 * v));
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      float g[8];
+      unpack8(load8(a.gate + sp.m * a.mod_rs + 8 * v), g);
+      stage_put(lds, v, g);
     }
     __syncthreads();
   }
@@ -495,22 +531,23 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_residual_gate
     V8 rv[NC], yv[NC], gv[NC];
     load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
     load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
-    const int64_t m = r / a.per_mod;
-    if (STAGED)
-      lds_row<NC>(gv, lds + (int)(m - ms.m0) * kRow, lane, dim);
-    else
-      load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
+    if (!STAGED) load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (!valid<NC>(c, lane, dim)) continue;
+      float g[8];
+      if (STAGED)
+        stage_get(lds, c, lane, g);
+      else
+        unpack8(gv[c], g);
       V8 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float g0 = lo(gv[c].w[k]) * lo(yv[c].w[k]);
-        float g1 = hi(gv[c].w[k]) * hi(yv[c].w[k]);
-        round2(g0, g1);
-        o.w[k] = pack(lo(rv[c].w[k]) + g0, hi(rv[c].w[k]) + g1);
+        float q0 = g[2 * k] * lo(yv[c].w[k]), q1 = g[2 * k + 1] * hi(yv[c].w[k]);
+        round2(q0, q1);                                         // bf(gate * y)
+        o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
       }
       store8(orow + 512 * c + 8 * lane, o);
     }
@@ -518,25 +555,38 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_residual_gate
 }
 
 // ---------------------------------------------------------------------------
-// Launch shape.
+// Launch shapes.
 //   Each wave gets a run of up to max_run rows, aiming at about kTargetWaves
-//   waves (MI355X: 256 CUs x 4 SIMDs x 4).  Modulation is staged in LDS when
-//   every workgroup's 4 * rows_per_wave rows meet at most two modulation
-//   rows (per-batch modulation); otherwise each wave loads it (per-token).
+//   waves (MI355X: 256 CUs x 4 SIMDs x 4).  Per-batch modulation (at least
+//   one workgroup's worth of rows per modulation row) takes the staged
+//   layout: blocks_per_mod workgroups per modulation row, each converting
+//   its modulation operands into LDS once.  Otherwise (per-token
+//   modulation) rows are laid out consecutively and each wave loads them.
 // ---------------------------------------------------------------------------
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMaxRun = 4;
 
+// Staging several binary32 rows stops paying once it limits the workgroups
+// per CU; above this LDS size the waves load the operands themselves.
+constexpr size_t kMaxStagedLds = 64 * 1024;
+
 struct Shape {
-  int64_t rows_per_wave;
+  int64_t rows_per_wave, blocks_per_mod;
   bool staged;
   dim3 grid;
 };
 
+// LDS bytes of `rows` binary32 staged rows.
+static size_t stage_bytes(int64_t dim, int rows) {
+  return (size_t)rows * (size_t)((dim + 511) / 512) * 128 * sizeof(float4);
+}
+
 // max_run: 1 for the kernels whose per-row work is cheap (measured fastest
 // with one row per wave); kMaxRun where staged per-batch work (tanh) is
-// worth sharing across more rows.
-static Shape row_shape(int64_t rows, int64_t per_mod, int64_t max_run) {
+// worth sharing across more rows.  staged_rows: binary32 rows the staged
+// layout keeps in LDS.
+static Shape row_shape(int64_t rows, int64_t per_mod, int64_t max_run, int64_t dim,
+                       int staged_rows) {
   Shape s;
   s.rows_per_wave = (rows + kTargetWaves - 1) / kTargetWaves;
   if (s.rows_per_wave > max_run) s.rows_per_wave = max_run;
@@ -544,12 +594,20 @@ static Shape row_shape(int64_t rows, int64_t per_mod, int64_t max_run) {
   if (const char *e = getenv("DIT_ROWS_PER_WAVE")) s.rows_per_wave = atoll(e);
 #endif
   if (s.rows_per_wave < 1) s.rows_per_wave = 1;
-  s.staged = per_mod >= kWavesPerBlock * s.rows_per_wave;
+  const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
+  s.staged = per_mod >= wg_rows && stage_bytes(dim, staged_rows) <= kMaxStagedLds;
 #ifdef DIT_TUNING
   if (getenv("DIT_NO_STAGING")) s.staged = false;
 #endif
-  const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
-  s.grid = dim3((unsigned)((rows + wg_rows - 1) / wg_rows));
+  const int64_t blocks_per_mod = (per_mod + wg_rows - 1) / wg_rows;
+  if (s.staged && rows / per_mod * blocks_per_mod > 0x7FFFFFFF) s.staged = false;
+  if (s.staged) {
+    s.blocks_per_mod = blocks_per_mod;
+    s.grid = dim3((unsigned)(rows / per_mod * blocks_per_mod));
+  } else {
+    s.blocks_per_mod = 0;
+    s.grid = dim3((unsigned)((rows + wg_rows - 1) / wg_rows));
+  }
   return s;
 }
 
@@ -566,43 +624,36 @@ static Shape row_shape(int64_t rows, int64_t per_mod, int64_t max_run) {
     return hipGetLastError();                   \
   } while (0)
 
-// LDS bytes of `rows` staged rows of NC vectors each.
-static size_t lds_bytes(int64_t dim, int rows) {
-  return (size_t)rows * (size_t)((dim + 511) / 512) * 64 * sizeof(uint4);
-}
+// The staged (KT) or unstaged (KF) instantiation, with its LDS bytes.
+#define DIT_ROW_LAUNCH(KT, KF, shm_t, shm_f)                        \
+  if (sh.staged)                                                    \
+    DIT_LAUNCH(KT, sh.grid, dim3(kThreads), shm_t, s, a);           \
+  else                                                              \
+    DIT_LAUNCH(KF, sh.grid, dim3(kThreads), shm_f, s, a);
 
 template <int MODE>
 static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, 1);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1, a.dim, 2);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = sh.staged ? lds_bytes(a.dim, 4) : 0;
-#define X(N)                                                                          \
-  case N:                                                                             \
-    if (sh.staged)                                                                    \
-      DIT_LAUNCH((k_ln_modulate<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
-    else                                                                              \
-      DIT_LAUNCH((k_ln_modulate<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a);  \
+  a.blocks_per_mod = sh.blocks_per_mod;
+#define X(N)                                                                              \
+  case N:                                                                                 \
+    DIT_ROW_LAUNCH((k_ln_modulate<N, MODE, true>), (k_ln_modulate<N, MODE, false>),       \
+                   stage_bytes(a.dim, 2), 0);                                             \
     break;
   DIT_ROW_DISPATCH();
 #undef X
 }
 
-// Staging three modulation rows per slot stops paying once it limits the
-// workgroups per CU; above this LDS size the wave loads them itself.
-constexpr size_t kMaxStagedLds = 64 * 1024;
-
 template <int MODE>
 static hipError_t gate_ln_dispatch(GateLnArgs a, hipStream_t s) {
-  Shape sh = row_shape(a.rows, a.per_mod, 1);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1, a.dim, 3);
   a.rows_per_wave = sh.rows_per_wave;
-  if (lds_bytes(a.dim, 6) > kMaxStagedLds) sh.staged = false;
-  const size_t shm = sh.staged ? lds_bytes(a.dim, 6) : 0;
-#define X(N)                                                                                 \
-  case N:                                                                                    \
-    if (sh.staged)                                                                           \
-      DIT_LAUNCH((k_gate_add_ln_modulate<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
-    else                                                                                     \
-      DIT_LAUNCH((k_gate_add_ln_modulate<N, MODE, false>), sh.grid, dim3(kThreads), 0, s, a); \
+  a.blocks_per_mod = sh.blocks_per_mod;
+#define X(N)                                                                     \
+  case N:                                                                        \
+    DIT_ROW_LAUNCH((k_gate_add_ln_modulate<N, MODE, true>),                      \
+                   (k_gate_add_ln_modulate<N, MODE, false>), stage_bytes(a.dim, 3), 0); \
     break;
   DIT_ROW_DISPATCH();
 #undef X
@@ -610,15 +661,13 @@ static hipError_t gate_ln_dispatch(GateLnArgs a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, 1);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1, a.dim, 2);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1);
-#define X(N)                                                                            \
-  case N:                                                                               \
-    if (sh.staged)                                                                      \
-      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, a); \
-    else                                                                                \
-      DIT_LAUNCH((k_rmsnorm_scale<N, MODE, false>), sh.grid, dim3(kThreads), shm, s, a); \
+  a.blocks_per_mod = sh.blocks_per_mod;
+#define X(N)                                                                              \
+  case N:                                                                                 \
+    DIT_ROW_LAUNCH((k_rmsnorm_scale<N, MODE, true>), (k_rmsnorm_scale<N, MODE, false>),   \
+                   stage_bytes(a.dim, 2), stage_bytes(a.dim, 1));                         \
     break;
   DIT_ROW_DISPATCH();
 #undef X
@@ -626,32 +675,28 @@ static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, kMaxRun);
+  const Shape sh = row_shape(a.rows, a.per_mod, kMaxRun, a.dim, 2);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = lds_bytes(a.dim, sh.staged ? 3 : 1) + kTanhTabVecs * sizeof(uint4);
-#define X(N)                                                                                  \
-  case N:                                                                                     \
-    if (sh.staged)                                                                            \
-      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, true>), sh.grid, dim3(kThreads), shm, s, \
-                 a);                                                                          \
-    else                                                                                      \
-      DIT_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, false>), sh.grid, dim3(kThreads), shm, s, \
-                 a);                                                                          \
+  a.blocks_per_mod = sh.blocks_per_mod;
+  const size_t tab = kTanhTabVecs * sizeof(uint4);
+#define X(N)                                                                          \
+  case N:                                                                             \
+    DIT_ROW_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, true>),                          \
+                   (k_rmsnorm_tanh_residual<N, MODE, false>),                         \
+                   stage_bytes(a.dim, 2) + tab, stage_bytes(a.dim, 1) + tab);         \
     break;
   DIT_ROW_DISPATCH();
 #undef X
 }
 
 static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, 1);
+  const Shape sh = row_shape(a.rows, a.per_mod, 1, a.dim, 1);
   a.rows_per_wave = sh.rows_per_wave;
-  const size_t shm = sh.staged ? lds_bytes(a.dim, 2) : 0;
+  a.blocks_per_mod = sh.blocks_per_mod;
 #define X(N)                                                                              \
   case N:                                                                                 \
-    if (sh.staged)                                                                        \
-      DIT_LAUNCH((k_residual_gate_add<N, true>), sh.grid, dim3(kThreads), shm, s, a);    \
-    else                                                                                  \
-      DIT_LAUNCH((k_residual_gate_add<N, false>), sh.grid, dim3(kThreads), 0, s, a);     \
+    DIT_ROW_LAUNCH((k_residual_gate_add<N, true>), (k_residual_gate_add<N, false>),       \
+                   stage_bytes(a.dim, 1), 0);                                             \
     break;
   DIT_ROW_DISPATCH();
 #undef X
