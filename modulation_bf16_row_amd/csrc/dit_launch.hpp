@@ -88,6 +88,7 @@ struct QkvArgs {
   int64_t batch, heads, s_total;
   float eps;
   int64_t tokens_per_wave;     // set by the launcher
+  int64_t parts;               // set by the launcher: waves sharing one token's heads
 };
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s);

@@ -3,13 +3,15 @@
 // of text and image tokens into joint Q/K/V buffers (page
 // "基于Agent的SGLang扩散模型Kernel优化实践", section "合并QKV投影时的数值问题").
 //
-// Geometry: a 64-lane wave handles one (batch, joint token) at a time and
-// walks a contiguous run of `tokens_per_wave` of them (one, unless the
-// problem is huge).  Within a token the wave covers four heads at
-// a time: lanes 16g..16g+15 hold head 4i+g, each lane 8 elements (128-bit
-// access), so a wave-wide access is 1 KiB of the token's row.  Each lane's
-// four RoPE pairs (4r .. 4r+3 for r = lane % 16) have their cos/sin loaded
-// once per token and reused for every head.
+// Geometry: the heads of one (batch, joint token) are split into `parts`
+// runs of HG head groups, one wave each; a wave walks a contiguous run of
+// `tokens_per_wave` tokens (one, unless the problem is huge).  Lanes
+// 16g..16g+15 hold head 4(p HG + i) + g of part p, each lane 8 elements
+// (128-bit access), so a wave-wide access is 1 KiB of the token's row.
+// Each lane's four RoPE pairs (4r .. 4r+3 for r = lane % 16) have their
+// cos/sin loaded once per token and part and reused for every head.
+// Splitting a token over several waves trades a few repeated cos/sin and
+// weight reads (cache hits) for fewer VGPRs per wave and more waves.
 #include <stdlib.h>
 
 #include "dit_device.hpp"
@@ -67,8 +69,8 @@ struct Token {
 };
 
 template <int HG>
-__device__ __forceinline__ void load_token(Token<HG> &t, const QkvArgs &a, int64_t tok, int g,
-                                           int r) {
+__device__ __forceinline__ void load_token(Token<HG> &t, const QkvArgs &a, int64_t tok, int g0,
+                                           int g, int r) {
   const int64_t b = tok / a.s_total;
   const int64_t jt = tok - b * a.s_total;
   const bool is_txt = jt < a.txt.tokens;
@@ -77,7 +79,7 @@ __device__ __forceinline__ void load_token(Token<HG> &t, const QkvArgs &a, int64
   const int64_t src = b * st.batch_stride + s * st.tok_stride + 8 * r;
 #pragma unroll
   for (int i = 0; i < HG; ++i) {
-    const int h = 4 * i + g;
+    const int h = 4 * (g0 + i) + g;
     if (h < a.heads) {
       t.q[i] = load8_stream(st.q + src + h * kHeadDim);
       t.k[i] = load8_stream(st.k + src + h * kHeadDim);
@@ -99,18 +101,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int lane = threadIdx.x & 63;
   const int64_t total = a.batch * a.s_total;
   const int64_t w = (int64_t)blockIdx.x * kQkvWaves + (threadIdx.x >> 6);
-  const int64_t t0 = w * a.tokens_per_wave;
+  const int64_t run = w / a.parts;
+  const int part = (int)(w - run * a.parts);
+  const int64_t t0 = run * a.tokens_per_wave;
   if (t0 >= total) return;
   const int64_t t1 = t0 + a.tokens_per_wave < total ? t0 + a.tokens_per_wave : total;
+  const int g0 = part * HG;          // first head group of this part
   const int g = lane >> 4;           // head within the group of four
   const int r = lane & 15;           // 8-element slice of the head
 
   for (int64_t t = t0; t < t1; ++t) {
     Token<HG> cur;
-    load_token<HG>(cur, a, t, g, r);
+    load_token<HG>(cur, a, t, g0, g, r);
 #pragma unroll
     for (int i = 0; i < HG; ++i) {
-      const int h = 4 * i + g;
+      const int h = 4 * (g0 + i) + g;
       // Lanes of absent heads (h >= heads) fill whole 16-lane groups of
       // their own, so the group sums of present heads never read them.
       if (h < a.heads) {
@@ -124,20 +129,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
 }
 
-// One token per wave measured fastest at the Qwen-Image shape (9216 tokens);
-// runs only start above ~1M tokens, to bound the grid.
+// One token per wave run; runs only start above ~1M tokens, to bound the
+// grid.  Head groups per wave: at most kQkvGroups (HG), the token's
+// ceil(heads / 4) groups split into as few equal parts as that allows.  At
+// the Qwen-Image shape (24 heads) one group per wave (70 VGPRs, 7 waves per
+// SIMD) measured 57.3 us against 58.4, 59.8 and 64.4 us for 2, 3 and 6.
 constexpr int64_t kQkvTargetWaves = int64_t(1) << 20;
+constexpr int kQkvGroups = 1;
 
 template <int MODE>
 static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {
   const int64_t total = a.batch * a.s_total;
   a.tokens_per_wave = (total + kQkvTargetWaves - 1) / kQkvTargetWaves;
+  const int groups = (int)((a.heads + 3) / 4);
+  int max_hg = kQkvGroups;
 #ifdef DIT_TUNING
   if (const char *e = getenv("DIT_TOKENS_PER_WAVE")) a.tokens_per_wave = atoll(e);
+  if (const char *e = getenv("DIT_QKV_GROUPS")) max_hg = atoi(e);
 #endif
-  const int64_t waves = (total + a.tokens_per_wave - 1) / a.tokens_per_wave;
+  a.parts = (groups + max_hg - 1) / max_hg;
+  const int hg = (groups + (int)a.parts - 1) / (int)a.parts;
+  const int64_t waves = (total + a.tokens_per_wave - 1) / a.tokens_per_wave * a.parts;
   const dim3 grid((unsigned)((waves + kQkvWaves - 1) / kQkvWaves));
-  switch ((int)((a.heads + 3) / 4)) {
+  switch (hg) {
 #define X(N) \
   case N: DIT_LAUNCH((k_qk_norm_rope<N, MODE>), grid, dim3(256), 0, s, a); break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
