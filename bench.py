@@ -24,6 +24,9 @@ names; per-kernel durations (mean, median, p10, p90) come from further steps
 launched eagerly from prepared calls, each dispatch recording its own
 start/stop events, in blocks that interleave the two modes (main, other,
 other, main); the other mode's figures are reported beside them.
+Beside the step, the fused gated residual + LN producer and the Wan 720p
+block's kernels (75600 x 5120, per-token modulation) are timed on their own,
+the latter with 8 sampled rows of each output checked against the oracle.
 The CPU baseline runs the oracle (plain C) over one full step on the host,
 single-threaded (the reported value) and on all threads of the process's
 CPU share (row blocks in parallel), and compares the GPU's outputs with it
@@ -198,6 +201,91 @@ def time_producers(m, torch, sets, mode, steps):
                     rows_per_s=float("%.4g" % (ROWS / (us * 1e-6))),
                     unfused_pair_us=round(pair_us, 2),
                     note="back to back; replaces residual_gate_add + ln_modulate")}
+
+
+# Wan 2.x 720p video block: 21 x 45 x 80 = 75600 latent tokens, hidden 5120.
+WAN_ROWS, WAN_D = 75600, 5120
+WAN_BYTES = {
+    "ln_modulate_per_token": 4 * WAN_ROWS * WAN_D * 2,                       # x, out; scale, shift
+    "rmsnorm_tanh_residual_per_token": 4 * WAN_ROWS * WAN_D * 2 + WAN_D * 2,  # x, res, out, gate; w
+    "rmsnorm_tanh_residual_per_batch": 3 * WAN_ROWS * WAN_D * 2 + 2 * WAN_D * 2,
+}
+
+
+def time_wan(m, torch, mode, reps=10, sample=8):
+    """The Wan 720p kernels at full size: two rotating input sets (~9 GB, far
+    beyond the Infinity Cache) drawn on the device from a seeded generator
+    (N(0, 1) rows, N(0, 0.1) modulation, U(0.5, 1.5) weight, the workload's
+    distributions; host generation of 774 MB tensors would dominate the
+    run), each dispatch timed by its own events; `sample` rows of every
+    output are checked bit for bit against the oracle."""
+    import oracle
+    R, Dw = WAN_ROWS, WAN_D
+    gen = torch.Generator(device="cuda").manual_seed(4000)
+
+    def bf(shape, std):
+        return (torch.randn(shape, device="cuda", generator=gen) * std).to(torch.bfloat16)
+
+    sets = []
+    for _ in range(2):
+        sets.append(dict(x=bf((R, Dw), 1.0), res=bf((R, Dw), 1.0), sc=bf((R, Dw), 0.1),
+                         sh=bf((R, Dw), 0.1), gt=bf((R, Dw), 0.1), g1=bf((1, Dw), 0.1),
+                         w=(torch.rand(Dw, device="cuda", generator=gen) + 0.5).to(
+                             torch.bfloat16),
+                         out=torch.empty((R, Dw), dtype=torch.bfloat16, device="cuda")))
+    ops = {
+        "ln_modulate_per_token": lambda s: m.dit_ln_modulate(
+            s["x"], s["sc"], s["sh"], EPS, mode, out=s["out"], prepare=True),
+        "rmsnorm_tanh_residual_per_token": lambda s: m.dit_rmsnorm_tanh_residual(
+            s["x"], s["res"], s["w"], s["gt"], EPS, mode, out=s["out"], prepare=True),
+        "rmsnorm_tanh_residual_per_batch": lambda s: m.dit_rmsnorm_tanh_residual(
+            s["x"], s["res"], s["w"], s["g1"], EPS, mode, out=s["out"], prepare=True),
+    }
+    rows = np.linspace(0, R - 1, sample).astype(np.int64)
+
+    def host(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    res = {}
+    for k, mk in ops.items():
+        plans = [mk(s) for s in sets]
+        for i in range(3):
+            plans[i % 2]()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            m.dit_time_next_launch(*ev[i])
+            plans[i % 2]()
+        torch.cuda.synchronize()
+        us_list = [1000.0 * a.elapsed_time(b) for a, b in ev]
+        us = float(np.mean(us_list))
+        gbs = WAN_BYTES[k] / (us * 1e-6) / 1e9
+        exact = None
+        if mode == "lossless":
+            s = sets[(reps - 1) % 2]
+            idx = torch.from_numpy(rows).cuda()
+            sel = {n: host(s[n].index_select(0, idx)) for n in ("x", "res", "sc", "sh", "gt",
+                                                               "out")}
+            if k == "ln_modulate_per_token":
+                ref = oracle.ln_modulate(sel["x"], sel["sc"], sel["sh"], EPS)
+            elif k == "rmsnorm_tanh_residual_per_token":
+                ref = oracle.rmsnorm_tanh_residual(sel["x"], sel["res"], host(s["w"]), sel["gt"],
+                                                   EPS)
+            else:
+                ref = oracle.rmsnorm_tanh_residual(sel["x"], sel["res"], host(s["w"]),
+                                                   host(s["g1"]), EPS)
+            exact = bool(np.array_equal(sel["out"], ref))
+        res[k] = dict(us=round(us, 2), median_us=round(float(np.median(us_list)), 2),
+                      bytes=WAN_BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
+                      rows_per_s=float("%.4g" % (R / (us * 1e-6))),
+                      bit_exact_sampled_rows=exact)
+        del plans
+    del sets
+    torch.cuda.empty_cache()
+    return res
 
 
 def _row_blocks(rows, mod_rows, n):
@@ -453,6 +541,7 @@ def main():
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
         producers=time_producers(m, torch, sets, args.mode, args.steps),
+        wan720p=time_wan(m, torch, args.mode),
         copy_ceiling_gbs=copy_ceiling(m, torch),
     )
     if not args.no_cpu:
