@@ -21,6 +21,7 @@ _lib = None
 
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64
 
@@ -83,6 +84,20 @@ def load(path=None):
                                      _f32p, _f32p, _i64, _i64, _i64, ctypes.c_float]
     lib.orc_bf16_round_array.argtypes = [_f32p, _u16p, _i64]
     lib.orc_bf16_round_bits_range.argtypes = [ctypes.c_uint32, _i64, _u16p]
+    lib.orc_e4m3.restype = ctypes.c_uint8
+    lib.orc_e4m3.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_array.argtypes = [_f32p, _u8p, _i64]
+    lib.orc_e4m3_bits_range.argtypes = [ctypes.c_uint32, _i64, _u8p]
+    lib.orc_ln_modulate_fp8.restype = ctypes.c_int
+    lib.orc_ln_modulate_fp8.argtypes = [_u16p, _i64, _u8p, _i64, _u16p, _i64, _u16p, _u16p, _i64,
+                                        _i64, _i64, _i64, ctypes.c_float, ctypes.c_float]
+    lib.orc_gate_add_ln_modulate_fp8.restype = ctypes.c_int
+    lib.orc_gate_add_ln_modulate_fp8.argtypes = [_u16p, _i64, _u16p, _i64, _u8p, _i64, _u16p,
+                                                 _i64, _u16p, _i64, _u16p, _u16p, _u16p, _i64,
+                                                 _i64, _i64, _i64, ctypes.c_float,
+                                                 ctypes.c_float]
     for name in ("orc_tanh_array", "orc_one_plus_array", "orc_rms_rstd_array"):
         getattr(lib, name).argtypes = [_u16p, _u16p, _i64]
     lib.orc_tanh_check_ld.argtypes = [_u16p, _u16p, _f64p, _i64]
@@ -128,6 +143,33 @@ def bf16_round(v):
     a = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
     out = np.empty(a.shape, dtype=np.uint16)
     lib.orc_bf16_round_array(_p32(a), _p16(out), a.size)
+    return out
+
+
+def _p8(a):
+    assert a.dtype == np.uint8
+    return a.ctypes.data_as(_u8p)
+
+
+def e4m3(v):
+    """binary32 -> OCP E4M3 codes (uint8; round to nearest even, saturating
+    at 448, NaN kept)."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    out = np.empty(a.shape, dtype=np.uint8)
+    load().orc_e4m3_array(_p32(a), _p8(out), a.size)
+    return out
+
+
+def e4m3_value(codes):
+    """E4M3 codes -> their values (float64)."""
+    lib = load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e4m3_value(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e4m3_bits_range(first, n):
+    out = np.empty(n, dtype=np.uint8)
+    load().orc_e4m3_bits_range(ctypes.c_uint32(first), n, _p8(out))
     return out
 
 
@@ -294,6 +336,40 @@ def gate_add_ln_modulate(residual, y, gate, scale, shift, eps=1e-6):
                                            _p16(shift), m_rs, gate.shape[0], rows, dim,
                                            ctypes.c_float(eps)))
     return out_res, out
+
+
+def ln_modulate_fp8(x, scale, shift, eps=1e-6, fp8_scale=1.0):
+    """(out, out8): LN + AdaLN modulate and E4M3(out / fp8_scale)."""
+    x_rs, x = _rows(x)
+    rows, dim = x.shape
+    m_rs, scale = _mod(scale, dim)
+    m_rs2, shift = _mod(shift, dim)
+    assert m_rs == m_rs2 and scale.shape == shift.shape
+    out = np.empty((rows, dim), dtype=np.uint16)
+    out8 = np.empty((rows, dim), dtype=np.uint8)
+    _check(load().orc_ln_modulate_fp8(_p16(out), dim, _p8(out8), dim, _p16(x), x_rs, _p16(scale),
+                                      _p16(shift), m_rs, scale.shape[0], rows, dim,
+                                      ctypes.c_float(eps), ctypes.c_float(fp8_scale)))
+    return out, out8
+
+
+def gate_add_ln_modulate_fp8(residual, y, gate, scale, shift, eps=1e-6, fp8_scale=1.0):
+    """(r', out, out8): the gated residual + LN + AdaLN producer and
+    E4M3(out / fp8_scale)."""
+    r_rs, residual = _rows(residual)
+    y_rs, y = _rows(y)
+    rows, dim = residual.shape
+    m_rs, gate = _mod(gate, dim)
+    _, scale = _mod(scale, dim)
+    _, shift = _mod(shift, dim)
+    out_res = np.empty((rows, dim), dtype=np.uint16)
+    out = np.empty((rows, dim), dtype=np.uint16)
+    out8 = np.empty((rows, dim), dtype=np.uint8)
+    _check(load().orc_gate_add_ln_modulate_fp8(
+        _p16(out_res), dim, _p16(out), dim, _p8(out8), dim, _p16(residual), r_rs, _p16(y), y_rs,
+        _p16(gate), _p16(scale), _p16(shift), m_rs, gate.shape[0], rows, dim,
+        ctypes.c_float(eps), ctypes.c_float(fp8_scale)))
+    return out_res, out, out8
 
 
 def _stream(q, k, v, qw, kw):

@@ -328,6 +328,87 @@ int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *ou
 }
 
 /* ------------------------------------------------------------------------- */
+/* BF16 + static E4M3 dual-output producers                                  */
+/* [P1 将FP8量化融合到前序算子: LayerNorm/AdaLN and gated residual +            */
+/*  LayerNorm/AdaLN also write a statically scaled E4M3 copy of their BF16     */
+/*  output, with an exact division by the scale]                             */
+/* ------------------------------------------------------------------------- */
+
+/* OCP E4M3 (no infinities): sign, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Code c (0 <= c <= 0x7E) has magnitude (c & 7) * 2^-9 when c < 8
+ * (subnormal) and (8 + (c & 7)) * 2^((c >> 3) - 10) otherwise; 0x7F is NaN. */
+double orc_e4m3_value(uint8_t c) {
+  const int m = c & 7, e = (c >> 3) & 15;
+  double v;
+  if ((c & 0x7F) == 0x7F) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+/* binary32 -> E4M3: the nearest of the 127 non-negative finite codes (binary
+ * search over their increasing magnitudes), ties to the even code; beyond the
+ * largest finite value (448) the result saturates at 448; NaN stays NaN
+ * (0x7F with the sign).  Zero and values that round to zero keep their sign. */
+uint8_t orc_e4m3(float v) {
+  const uint8_t sign = (f32_bits(v) >> 31) ? 0x80 : 0x00;
+  if (v != v) return (uint8_t)(sign | 0x7F);
+  const double a = fabs((double)v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  int lo = 0, hi = 0x7E;               /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (orc_e4m3_value((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const double dl = a - orc_e4m3_value((uint8_t)lo), dh = orc_e4m3_value((uint8_t)hi) - a;
+  int c = lo;
+  if (dh < dl || (dh == dl && (hi & 1) == 0)) c = hi;
+  return (uint8_t)(sign | c);
+}
+
+/* q = E4M3(bf16 value of h / scale) with an IEEE binary32 division. */
+static uint8_t quant(uint16_t h, float scale) { return orc_e4m3(orc_bf16_value(h) / scale); }
+
+int orc_ln_modulate_fp8(uint16_t *out, int64_t out_rs, uint8_t *out8, int64_t out8_rs,
+                        const uint16_t *x, int64_t x_rs, const uint16_t *scale,
+                        const uint16_t *shift, int64_t mod_rs, int64_t mod_rows, int64_t rows,
+                        int64_t dim, float eps, float fp8_scale) {
+  if (orc_ln_modulate(out, out_rs, x, x_rs, scale, shift, mod_rs, mod_rows, rows, dim, eps))
+    return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < dim; ++i) out8[r * out8_rs + i] = quant(out[r * out_rs + i], fp8_scale);
+  return 0;
+}
+
+int orc_gate_add_ln_modulate_fp8(uint16_t *out_res, int64_t out_res_rs, uint16_t *out,
+                                 int64_t out_rs, uint8_t *out8, int64_t out8_rs,
+                                 const uint16_t *residual, int64_t res_rs, const uint16_t *y,
+                                 int64_t y_rs, const uint16_t *gate, const uint16_t *scale,
+                                 const uint16_t *shift, int64_t mod_rs, int64_t mod_rows,
+                                 int64_t rows, int64_t dim, float eps, float fp8_scale) {
+  if (orc_gate_add_ln_modulate(out_res, out_res_rs, out, out_rs, residual, res_rs, y, y_rs, gate,
+                               scale, shift, mod_rs, mod_rows, rows, dim, eps))
+    return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < dim; ++i) out8[r * out8_rs + i] = quant(out[r * out_rs + i], fp8_scale);
+  return 0;
+}
+
+void orc_e4m3_array(const float *in, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3(in[i]);
+}
+
+/* E4M3 codes of every binary32 bit pattern first .. first + n - 1. */
+void orc_e4m3_bits_range(uint32_t first, int64_t n, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3(bits_f32(first + (uint32_t)i));
+}
+
+/* ------------------------------------------------------------------------- */
 /* Q/K RMSNorm + interleaved RoPE + joint QKV write                          */
 /* [P1 合并QKV投影时的数值问题: the four steps of the epilogue]                 */
 /* ------------------------------------------------------------------------- */

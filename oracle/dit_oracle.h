@@ -50,6 +50,21 @@ int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *ou
                              const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
                              int64_t mod_rows, int64_t rows, int64_t dim, float eps);
 
+double orc_e4m3_value(uint8_t c);
+uint8_t orc_e4m3(float v);
+int orc_ln_modulate_fp8(uint16_t *out, int64_t out_rs, uint8_t *out8, int64_t out8_rs,
+                        const uint16_t *x, int64_t x_rs, const uint16_t *scale,
+                        const uint16_t *shift, int64_t mod_rs, int64_t mod_rows, int64_t rows,
+                        int64_t dim, float eps, float fp8_scale);
+int orc_gate_add_ln_modulate_fp8(uint16_t *out_res, int64_t out_res_rs, uint16_t *out,
+                                 int64_t out_rs, uint8_t *out8, int64_t out8_rs,
+                                 const uint16_t *residual, int64_t res_rs, const uint16_t *y,
+                                 int64_t y_rs, const uint16_t *gate, const uint16_t *scale,
+                                 const uint16_t *shift, int64_t mod_rs, int64_t mod_rows,
+                                 int64_t rows, int64_t dim, float eps, float fp8_scale);
+void orc_e4m3_array(const float *in, uint8_t *out, int64_t n);
+void orc_e4m3_bits_range(uint32_t first, int64_t n, uint8_t *out);
+
 typedef struct {
   const uint16_t *q, *k, *v;      /* [B, S, H, Dh] views, head stride Dh */
   int64_t tok_stride, batch_stride;

@@ -75,6 +75,18 @@ MUTANTS = {
         "scale + m * mod_rs, shift + m * mod_rs,",
         "scale + m * mod_rs, scale + m * mod_rs,",
         ["test_gate_add_ln_zero_gate_constant_residual"]),
+    "E4M3 ties away from zero": (
+        "if (dh < dl || (dh == dl && (hi & 1) == 0)) c = hi;",
+        "if (dh <= dl) c = hi;",
+        ["test_e4m3_midpoints_tie_to_even_and_saturate"]),
+    "E4M3 overflow to NaN": (
+        "if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
+        "if (a > 464.0) return (uint8_t)(sign | 0x7F);",
+        ["test_e4m3_midpoints_tie_to_even_and_saturate"]),
+    "FP8 scale by reciprocal": (
+        "return orc_e4m3(orc_bf16_value(h) / scale);",
+        "return orc_e4m3(orc_bf16_value(h) * (1.0f / scale));",
+        ["test_fp8_quantization_divides_by_the_scale"]),
     "RoPE sign": (
         "o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);",
         "o[2 * i] = orc_bf16_round(a * c[i] + b * z[i]);",

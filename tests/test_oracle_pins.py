@@ -590,6 +590,109 @@ def test_gate_add_ln_per_batch_equals_repeated_per_token():
 
 
 # --------------------------------------------------------------------------------------
+# BF16 + static E4M3 dual output (page "基于Agent的SGLang扩散模型Kernel优化实践", section
+# "将FP8量化融合到前序算子")
+# --------------------------------------------------------------------------------------
+
+E4M3_CODES = np.arange(256, dtype=np.uint32).astype(np.uint8)
+
+
+def _torch_e4m3(v):
+    """torch's CPU float8_e4m3fn conversion (round to nearest even) of |v| < 464."""
+    return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_codes_roundtrip_and_known_values():
+    vals = oracle.e4m3_value(E4M3_CODES)
+    fin = np.isfinite(vals)
+    assert fin.sum() == 254 and not fin[0x7F] and not fin[0xFF]
+    assert np.array_equal(oracle.e4m3(vals[fin].astype(np.float32)), E4M3_CODES[fin])
+    known = {1.0: 0x38, 0.5: 0x30, 448.0: 0x7E, 2.0 ** -9: 0x01, 2.0 ** -6: 0x08,
+             1.75: 0x3E, 240.0: 0x77, -2.0: 0xC0, 0.0: 0x00}
+    for v, c in known.items():
+        assert oracle.e4m3(np.float32(v)) == c, (v, hex(c))
+    assert oracle.e4m3(np.float32(-0.0)) == 0x80
+    # decoded magnitudes: 7 subnormals m * 2^-9, then (8 + m) * 2^(e - 10)
+    assert vals[0x07] == 7 * 2.0 ** -9 and vals[0x08] == 2.0 ** -6 and vals[0x7E] == 448.0
+
+
+def test_e4m3_midpoints_tie_to_even_and_saturate():
+    vals = oracle.e4m3_value(E4M3_CODES[:0x7F])
+    for c in range(0x7E):
+        mid = (vals[c] + vals[c + 1]) / 2                    # exact in binary32
+        m32 = np.float32(mid)
+        assert float(m32) == mid
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3(m32) == even, hex(c)
+        assert oracle.e4m3(np.nextafter(m32, np.float32(0))) == c
+        assert oracle.e4m3(np.nextafter(m32, np.float32(np.inf))) == c + 1
+        assert oracle.e4m3(-m32) == 0x80 | even
+    for v in (448.0, 460.0, 464.0, 500.0, 1e30, np.inf):
+        assert oracle.e4m3(np.float32(v)) == 0x7E and oracle.e4m3(np.float32(-v)) == 0xFE
+    assert oracle.e4m3(np.float32(np.nan)) & 0x7F == 0x7F
+    assert oracle.e4m3(np.float32(2.0 ** -10)) == 0x00        # tie with zero: even
+    assert oracle.e4m3(np.float32(-(2.0 ** -11))) == 0x80     # underflow keeps the sign
+
+
+def test_e4m3_vs_torch():
+    rng = np.random.default_rng(120)
+    n = 1 << 20
+    v = (rng.standard_normal(n) * np.exp2(rng.integers(-14, 9, n))).astype(np.float32)
+    v = v[np.abs(v) < 464]
+    assert np.array_equal(oracle.e4m3(v), _torch_e4m3(v))
+
+
+@pytest.mark.parametrize("fp8_scale", [1.0, 0.0173, 2.0 ** -3])
+def test_ln_modulate_fp8_vs_torch_quant(fp8_scale):
+    """The BF16 output is the plain LN + modulate output; the E4M3 output is
+    torch's IEEE division by the scale, clamped to +-448, cast to E4M3."""
+    x = synth.normal_bf16((12, 1032), 1.0, 121)
+    scale = synth.normal_bf16((2, 1032), 0.1, 122)
+    shift = synth.normal_bf16((2, 1032), 0.1, 123)
+    out, out8 = oracle.ln_modulate_fp8(x, scale, shift, 1e-6, fp8_scale)
+    assert np.array_equal(out, oracle.ln_modulate(x, scale, shift, 1e-6))
+    t = torch.from_numpy(value_of_bf16(out).astype(np.float32))
+    ref = (t / torch.tensor(fp8_scale, dtype=torch.float32)).clamp(-448, 448)
+    assert np.array_equal(out8, ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_fp8_quantization_divides_by_the_scale():
+    """Constant rows give out = shift, so out8 = E4M3(shift / s).  For s = 3.1
+    these bf16 values give a different E4M3 code when h / s is replaced by
+    h * (1 / s) (one binary32 ulp across a rounding midpoint); the division
+    decides."""
+    s = np.float32(3.1)
+    h = value_of_bf16(np.arange(65536, dtype=np.uint32).astype(np.uint16)).astype(np.float32)
+    fin = np.isfinite(h)
+    with np.errstate(all="ignore"):
+        by_div = oracle.e4m3((h / s).astype(np.float32))
+        by_rcp = oracle.e4m3((h * (np.float32(1) / s)).astype(np.float32))
+    pick = np.flatnonzero((by_div != by_rcp) & fin)[:64]
+    assert pick.size >= 8
+    D = 8 * ((pick.size + 7) // 8)
+    shift = np.full((1, D), 0x3F80, dtype=np.uint16)
+    shift[0, :pick.size] = pick.astype(np.uint16)
+    x = synth.constant_bf16((2, D), 0.75)
+    scale = np.zeros((1, D), dtype=np.uint16)
+    out, out8 = oracle.ln_modulate_fp8(x, scale, shift, 1e-6, float(s))
+    assert np.array_equal(out, np.repeat(shift, 2, axis=0))
+    assert np.array_equal(out8[:, :pick.size], np.repeat(by_div[pick][None], 2, axis=0))
+
+
+def test_gate_add_ln_modulate_fp8():
+    res = synth.normal_bf16((8, 520), 1.0, 124)
+    y = synth.normal_bf16((8, 520), 1.0, 125)
+    gate, scale, shift = (synth.normal_bf16((2, 520), 0.1, 126 + i) for i in range(3))
+    rp, out, out8 = oracle.gate_add_ln_modulate_fp8(res, y, gate, scale, shift, 1e-6, 0.05)
+    rp2, out2 = oracle.gate_add_ln_modulate(res, y, gate, scale, shift, 1e-6)
+    assert np.array_equal(rp, rp2) and np.array_equal(out, out2)
+    t = torch.from_numpy(value_of_bf16(out).astype(np.float32)) / torch.tensor(0.05)
+    assert np.array_equal(out8, t.clamp(-448, 448).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy())
+
+
+# --------------------------------------------------------------------------------------
 # Q/K RMSNorm + interleaved RoPE + joint write
 # --------------------------------------------------------------------------------------
 
