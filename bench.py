@@ -70,7 +70,12 @@ ROW_KERNELS = [k for k in KERNELS if k != "qk_norm_rope"]   # (rows, D) outputs
 PRODUCER_BYTES = {
     # residual, y, r', out; gate, scale, shift
     "gate_add_ln_modulate": 4 * ROWS * D * 2 + 3 * B * D * 2,
+    # x, out, E4M3 out; scale, shift; the fp8 scale
+    "ln_modulate_fp8": 2 * ROWS * D * 2 + ROWS * D + 2 * B * D * 2 + 4,
+    # residual, y, r', out, E4M3 out; gate, scale, shift; the fp8 scale
+    "gate_add_ln_modulate_fp8": 4 * ROWS * D * 2 + ROWS * D + 3 * B * D * 2 + 4,
 }
+FP8_SCALE = 0.0173    # static per-tensor scale of the E4M3 outputs
 
 
 def read_traffic(kernel):
@@ -166,8 +171,9 @@ def make_plans(m, s, mode):
 
 
 def time_producers(m, torch, sets, mode, steps):
-    """Each fused producer back to back over the two buffer sets, and the
-    unfused calls it replaces, each dispatch timed by its own events."""
+    """Each fused producer back to back over the two buffer sets (and, for
+    the gated residual + LN producer, the unfused pair it replaces), each
+    dispatch timed by its own events."""
     def run(calls):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls * steps]
         for a, b in ev:
@@ -182,25 +188,40 @@ def time_producers(m, torch, sets, mode, steps):
         us = [1000.0 * a.elapsed_time(b) for a, b in ev]
         return float(np.mean(us)) * len(calls), us
 
-    fused = [m.dit_gate_add_ln_modulate(s.res, s.y, s.gate, s.scale, s.shift, EPS, mode,
-                                        out_residual=s.prod["residual"], out=s.prod["out"],
-                                        prepare=True) for s in sets]
+    fs = torch.tensor([FP8_SCALE], dtype=torch.float32, device="cuda")
+    q8 = [torch.empty((ROWS, D), dtype=torch.float8_e4m3fn, device="cuda") for _ in sets]
+    plans = {
+        "gate_add_ln_modulate": [m.dit_gate_add_ln_modulate(
+            s.res, s.y, s.gate, s.scale, s.shift, EPS, mode, out_residual=s.prod["residual"],
+            out=s.prod["out"], prepare=True) for s in sets],
+        "ln_modulate_fp8": [m.dit_ln_modulate_fp8(
+            s.x, s.scale, s.shift, fs, EPS, mode, out=s.prod["out"], out_fp8=q, prepare=True)
+            for s, q in zip(sets, q8)],
+        "gate_add_ln_modulate_fp8": [m.dit_gate_add_ln_modulate_fp8(
+            s.res, s.y, s.gate, s.scale, s.shift, fs, EPS, mode,
+            out_residual=s.prod["residual"], out=s.prod["out"], out_fp8=q, prepare=True)
+            for s, q in zip(sets, q8)],
+    }
     gate = [m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.prod["residual"],
                                     prepare=True) for s in sets]
     ln = [m.dit_ln_modulate(s.prod["residual"], s.scale, s.shift, EPS, mode,
                             out=s.prod["out"], prepare=True) for s in sets]
-    run([fused])                                     # warm-up
-    us, samples = run([fused])
+    res = {}
+    for k, p in plans.items():
+        run([p])                                     # warm-up
+        us, samples = run([p])
+        gbs = PRODUCER_BYTES[k] / (us * 1e-6) / 1e9
+        res[k] = dict(us=round(us, 2), median_us=round(float(np.median(samples)), 2),
+                      p10_us=round(float(np.percentile(samples, 10)), 2),
+                      p90_us=round(float(np.percentile(samples, 90)), 2),
+                      bytes=PRODUCER_BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
+                      rows_per_s=float("%.4g" % (ROWS / (us * 1e-6))))
     pair_us, _ = run([gate, ln])
-    k = "gate_add_ln_modulate"
-    gbs = PRODUCER_BYTES[k] / (us * 1e-6) / 1e9
-    return {k: dict(us=round(us, 2), median_us=round(float(np.median(samples)), 2),
-                    p10_us=round(float(np.percentile(samples, 10)), 2),
-                    p90_us=round(float(np.percentile(samples, 90)), 2),
-                    bytes=PRODUCER_BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
-                    rows_per_s=float("%.4g" % (ROWS / (us * 1e-6))),
-                    unfused_pair_us=round(pair_us, 2),
-                    note="back to back; replaces residual_gate_add + ln_modulate")}
+    res["gate_add_ln_modulate"]["unfused_pair_us"] = round(pair_us, 2)
+    res["note"] = ("back to back; gate_add_ln_modulate replaces residual_gate_add + "
+                   "ln_modulate (unfused_pair_us); fp8 variants add an E4M3 copy, scale %g"
+                   % FP8_SCALE)
+    return res
 
 
 # Wan 2.x 720p video block: 21 x 45 x 80 = 75600 latent tokens, hidden 5120.

@@ -59,6 +59,19 @@ dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t
 dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
                             hipStream_t stream);
 
+typedef enum {
+  DIT_PROBE_E4M3 = 0,       /* out[i] = E4M3 code of the binary32 in[i]              */
+  DIT_PROBE_FP8_QUANT = 1   /* out[i] = E4M3 code of (bf16 in[i]) / *scale, as the
+                               dual-output producers quantize                      */
+} dit_probe_fp8_t;
+
+/* The E4M3 conversion of the dual-output producers (dit_producers.h) over an
+ * array: saturation to +-448, round to nearest even, NaN kept.  in: float
+ * (op 0) or bf16 (op 1) device array of n elements; scale: device pointer to
+ * one float (op 1 only; may be NULL for op 0). */
+dit_status_t dit_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

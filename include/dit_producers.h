@@ -43,6 +43,33 @@ dit_status_t dit_gate_add_ln_modulate(void *out_residual, int64_t out_res_rs, vo
                                       int64_t mod_rows, int64_t rows, int64_t dim, float eps,
                                       int mode, hipStream_t stream);
 
+/*
+ * BF16 + static E4M3 dual output  [P1 将FP8量化融合到前序算子]
+ * The producers above also write an OCP E4M3 copy of their BF16 output for
+ * an FP8 GEMM that follows:
+ *   out_fp8 = E4M3( bf16_value(out) / *fp8_scale )
+ * with a correctly rounded binary32 division (in both modes: the pages note
+ * that a reciprocal one binary32 ulp off moves codes across E4M3 rounding
+ * midpoints), E4M3 round to nearest even, values beyond +-448 saturated to
+ * +-448, NaN kept.  The BF16 outputs are exactly those of the BF16-only
+ * calls.
+ * out_fp8: [rows, dim] bytes, row stride out_fp8_rs bytes (a multiple of 8,
+ * >= dim), 8-byte aligned; it may overlap nothing else.
+ * fp8_scale: device pointer to one float (static per-tensor scale), read by
+ * the kernel, so a graph replay picks up a new value; 4-byte aligned.
+ */
+dit_status_t dit_ln_modulate_fp8(void *out, int64_t out_rs, void *out_fp8, int64_t out_fp8_rs,
+                                 const void *x, int64_t x_rs, const void *scale,
+                                 const void *shift, int64_t mod_rs, int64_t mod_rows,
+                                 int64_t rows, int64_t dim, float eps, const float *fp8_scale,
+                                 int mode, hipStream_t stream);
+
+dit_status_t dit_gate_add_ln_modulate_fp8(
+    void *out_residual, int64_t out_res_rs, void *out, int64_t out_rs, void *out_fp8,
+    int64_t out_fp8_rs, const void *residual, int64_t res_rs, const void *y, int64_t y_rs,
+    const void *gate, const void *scale, const void *shift, int64_t mod_rs, int64_t mod_rows,
+    int64_t rows, int64_t dim, float eps, const float *fp8_scale, int mode, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

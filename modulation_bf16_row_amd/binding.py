@@ -63,6 +63,11 @@ SIGNATURES = {
                               _vp],
     "dit_gate_add_ln_modulate": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
                                  _i64, _i64, _i64, _f32, _int, _vp],
+    "dit_ln_modulate_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                            _f32, _vp, _int, _vp],
+    "dit_gate_add_ln_modulate_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                     _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _int, _vp],
+    "dit_probe_fp8": [_int, _vp, _vp, _i64, _vp, _vp],
     "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
                          ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
     "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
@@ -115,11 +120,12 @@ def _stream(t):
     return _vp(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _flat_rows(t, name):
+def _flat_rows(t, name, byte=False):
     """(rows, row_stride) of a [..., dim] tensor whose outer dimensions fold
-    into one uniform row stride (the flat-row-stride rule)."""
-    if t.dtype != torch.bfloat16:
-        raise DitUnsupported(f"{name} must be bfloat16, got {t.dtype}")
+    into one uniform row stride (the flat-row-stride rule).  byte: a uint8
+    tensor (E4M3 codes) instead of bfloat16."""
+    if t.dtype != (torch.uint8 if byte else torch.bfloat16):
+        raise DitUnsupported(f"{name} must be {'uint8' if byte else 'bfloat16'}, got {t.dtype}")
     if t.device.type != "cuda":
         raise DitUnsupported(f"{name} must be on a ROCm device, got {t.device}")
     if t.dim() == 0:
@@ -283,6 +289,75 @@ def dit_gate_add_ln_modulate(residual, y, gate, scale, shift, eps=1e-6, mode="lo
                  mrows, rows, dim, eps, _mode(mode), _stream(residual))
 
 
+def _fp8_out(x, out_fp8):
+    """The E4M3 output (float8_e4m3fn or uint8, shaped like x) and its row
+    stride in bytes."""
+    if out_fp8 is None:
+        out_fp8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if out_fp8.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise DitUnsupported("out_fp8 must be float8_e4m3fn or uint8")
+    if out_fp8.shape != x.shape:
+        raise DitInvalid(f"out_fp8 has shape {tuple(out_fp8.shape)}, expected {tuple(x.shape)}")
+    if out_fp8.device != x.device:
+        raise DitInvalid("out_fp8 is on another device")
+    _, rs = _flat_rows(out_fp8.view(torch.uint8), "out_fp8", byte=True)
+    return out_fp8, rs
+
+
+def _fp8_scale(t, like):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.numel() != 1:
+        raise DitUnsupported("fp8_scale must be a one-element float32 tensor")
+    if t.device != like.device:
+        raise DitInvalid("fp8_scale is on another device")
+    return t
+
+
+def dit_ln_modulate_fp8(x, scale, shift, fp8_scale, eps=1e-6, mode="lossless", out=None,
+                        out_fp8=None, prepare=False):
+    """LN(x) * (1 + scale) + shift in BF16 and its E4M3 copy E4M3(out / fp8_scale).
+    fp8_scale: one-element float32 device tensor.  Returns (out, out_fp8)."""
+    _same_device(x, scale, shift)
+    rows, x_rs = _flat_rows(x, "x")
+    dim = x.shape[-1]
+    mrows, mrs = _mod_rows(scale, shift, dim, ("scale", "shift"))
+    out = _out_like(x, out)
+    _same_device(x, out)
+    _, o_rs = _flat_rows(out, "out")
+    out_fp8, q_rs = _fp8_out(x, out_fp8)
+    fs = _fp8_scale(fp8_scale, x)
+    return _call("dit_ln_modulate_fp8", (out, out_fp8), prepare, out.data_ptr(), o_rs,
+                 out_fp8.data_ptr(), q_rs, x.data_ptr(), x_rs, scale.data_ptr(),
+                 shift.data_ptr(), mrs, mrows, rows, dim, eps, fs.data_ptr(), _mode(mode),
+                 _stream(x))
+
+
+def dit_gate_add_ln_modulate_fp8(residual, y, gate, scale, shift, fp8_scale, eps=1e-6,
+                                 mode="lossless", out_residual=None, out=None, out_fp8=None,
+                                 prepare=False):
+    """The gated residual + LN + AdaLN producer with an E4M3 copy of its LN
+    output.  Returns (r', out, out_fp8)."""
+    _same_device(residual, y, gate, scale, shift)
+    rows, r_rs = _flat_rows(residual, "residual")
+    dim = residual.shape[-1]
+    if y.shape != residual.shape:
+        raise DitInvalid("y must have the shape of residual")
+    _, y_rs = _flat_rows(y, "y")
+    mrows, mrs = _mod_rows(gate, scale, dim, ("gate", "scale"))
+    _mod_rows(gate, shift, dim, ("gate", "shift"))
+    out_residual = _out_like(residual, out_residual)
+    out = _out_like(residual, out)
+    _same_device(residual, out_residual, out)
+    _, rr_rs = _flat_rows(out_residual, "out_residual")
+    _, o_rs = _flat_rows(out, "out")
+    out_fp8, q_rs = _fp8_out(residual, out_fp8)
+    fs = _fp8_scale(fp8_scale, residual)
+    return _call("dit_gate_add_ln_modulate_fp8", (out_residual, out, out_fp8), prepare,
+                 out_residual.data_ptr(), rr_rs, out.data_ptr(), o_rs, out_fp8.data_ptr(), q_rs,
+                 residual.data_ptr(), r_rs, y.data_ptr(), y_rs, gate.data_ptr(),
+                 scale.data_ptr(), shift.data_ptr(), mrs, mrows, rows, dim, eps, fs.data_ptr(),
+                 _mode(mode), _stream(residual))
+
+
 def _qkv_stream(st):
     """st: dict with q, k, v ([B, S, H, Dh] views sharing strides) and q_weight,
     k_weight ([Dh]); None means no tokens."""
@@ -376,6 +451,15 @@ def dit_probe_copy(dst, src, flags=0):
         raise DitInvalid("dst and src sizes differ")
     _check(lib().dit_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, flags, _stream(src)))
     return dst
+
+
+def dit_probe_fp8(op, inp, scale=None):
+    """op 0: E4M3 codes of a float32 tensor; op 1: E4M3 codes of a bfloat16
+    tensor divided by scale (one-element float32 tensor).  Returns uint8."""
+    out = torch.empty(inp.shape, dtype=torch.uint8, device=inp.device)
+    _check(lib().dit_probe_fp8(op, out.data_ptr(), inp.data_ptr(), inp.numel(),
+                               scale.data_ptr() if scale is not None else None, _stream(inp)))
+    return out
 
 
 def dit_probe_row_sum(t, head=False):

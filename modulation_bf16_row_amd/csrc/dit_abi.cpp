@@ -278,6 +278,105 @@ dit_status_t dit_gate_add_ln_modulate(void *out_residual, int64_t out_res_rs, vo
 
 namespace {
 
+// Checks of the E4M3 output of the dual-output producers: a byte row tensor
+// (8-byte aligned, row stride a multiple of 8 bytes) that overlaps no other
+// argument, and a 4-byte aligned scale that no output touches.
+dit_status_t check_fp8(void *out8, int64_t out8_rs, const float *fp8_scale, int64_t rows,
+                       int64_t dim, const Span *others, int n_others) {
+  if (!out8) return fail(DIT_ERR_INVALID, "out_fp8 is NULL");
+  if (!fp8_scale) return fail(DIT_ERR_INVALID, "fp8_scale is NULL");
+  if (out8_rs < 0) return fail(DIT_ERR_INVALID, "bad out_fp8 row stride");
+  if (rows > 1 && (out8_rs < dim || out8_rs % 8 != 0))
+    return fail(DIT_ERR_UNSUPPORTED, "bad out_fp8 row stride");
+  if ((reinterpret_cast<uintptr_t>(out8) & 7u) != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "out_fp8 is not 8-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(fp8_scale) & 3u) != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "fp8_scale is not 4-byte aligned");
+  const Span s8{reinterpret_cast<uintptr_t>(out8), out8_rs, rows, dim};
+  const Span sc{reinterpret_cast<uintptr_t>(fp8_scale), 0, 1, 4};
+  if (spans_overlap(s8, sc)) return fail(DIT_ERR_INVALID, "out_fp8 overlaps fp8_scale");
+  for (int i = 0; i < n_others; ++i) {
+    if (spans_overlap(s8, others[i])) return fail(DIT_ERR_INVALID, "out_fp8 overlaps a tensor");
+  }
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status_t dit_ln_modulate_fp8(void *out, int64_t out_rs, void *out_fp8, int64_t out_fp8_rs,
+                                 const void *x, int64_t x_rs, const void *scale,
+                                 const void *shift, int64_t mod_rs, int64_t mod_rows,
+                                 int64_t rows, int64_t dim, float eps, const float *fp8_scale,
+                                 int mode, hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(x, x_rs, rows, dim, "x is NULL", "bad x row stride"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(shift, mod_rs, mod_rows, dim, "shift is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(x, x_rs, rows, dim)};
+  const Span cs[] = {rows_span(scale, mod_rs, mod_rows, dim),
+                     rows_span(shift, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 1, cs, 2));
+  const Span sc{reinterpret_cast<uintptr_t>(fp8_scale), 0, 1, 4};
+  if (fp8_scale && spans_overlap(so, sc)) return fail(DIT_ERR_INVALID, "out overlaps fp8_scale");
+  const Span others[] = {so, ins[0], cs[0], cs[1]};
+  DIT_TRY(check_fp8(out_fp8, out_fp8_rs, fp8_scale, rows, dim, others, 4));
+  dit::LnModArgs a{static_cast<uint16_t *>(out), u16(x), u16(scale), u16(shift), out_rs, x_rs,
+                   mod_rs, rows, dim, rows / mod_rows, eps};
+  a.out8 = static_cast<uint8_t *>(out_fp8);
+  a.out8_rs = out_fp8_rs;
+  a.fp8_scale = fp8_scale;
+  return hip_status(dit::launch_ln_modulate(a, mode, stream));
+}
+
+dit_status_t dit_gate_add_ln_modulate_fp8(
+    void *out_residual, int64_t out_res_rs, void *out, int64_t out_rs, void *out_fp8,
+    int64_t out_fp8_rs, const void *residual, int64_t res_rs, const void *y, int64_t y_rs,
+    const void *gate, const void *scale, const void *shift, int64_t mod_rs, int64_t mod_rows,
+    int64_t rows, int64_t dim, float eps, const float *fp8_scale, int mode, hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out_residual, out_res_rs, rows, dim, "out_residual is NULL",
+                     "bad out_residual row stride"));
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(residual, res_rs, rows, dim, "residual is NULL", "bad residual row stride"));
+  DIT_TRY(check_rows(y, y_rs, rows, dim, "y is NULL", "bad y row stride"));
+  DIT_TRY(check_rows(gate, mod_rs, mod_rows, dim, "gate is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(shift, mod_rs, mod_rows, dim, "shift is NULL", "bad modulation row stride"));
+  const Span sr = rows_span(out_residual, out_res_rs, rows, dim);
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(residual, res_rs, rows, dim), rows_span(y, y_rs, rows, dim)};
+  const Span cs[] = {rows_span(gate, mod_rs, mod_rows, dim),
+                     rows_span(scale, mod_rs, mod_rows, dim),
+                     rows_span(shift, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(sr, ins, 2, cs, 3));
+  DIT_TRY(check_out_alias(so, ins, 2, cs, 3));
+  if (spans_overlap(sr, so)) return fail(DIT_ERR_INVALID, "the two outputs overlap");
+  const Span sc{reinterpret_cast<uintptr_t>(fp8_scale), 0, 1, 4};
+  if (fp8_scale && (spans_overlap(so, sc) || spans_overlap(sr, sc)))
+    return fail(DIT_ERR_INVALID, "an output overlaps fp8_scale");
+  const Span others[] = {sr, so, ins[0], ins[1], cs[0], cs[1], cs[2]};
+  DIT_TRY(check_fp8(out_fp8, out_fp8_rs, fp8_scale, rows, dim, others, 7));
+  dit::GateLnArgs a{static_cast<uint16_t *>(out_residual), static_cast<uint16_t *>(out),
+                    u16(residual), u16(y), u16(gate), u16(scale), u16(shift), out_res_rs, out_rs,
+                    res_rs, y_rs, mod_rs, rows, dim, rows / mod_rows, eps};
+  a.out8 = static_cast<uint8_t *>(out_fp8);
+  a.out8_rs = out_fp8_rs;
+  a.fp8_scale = fp8_scale;
+  return hip_status(dit::launch_gate_add_ln_modulate(a, mode, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
 // Segments of a [batch, tokens, heads*128] view with the given strides.
 Span token_span(const void *p, int64_t ts, int64_t bs, int64_t batch, int64_t tokens,
                 int64_t width) {
@@ -426,6 +525,17 @@ dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, i
   if (!out || !a || (op == DIT_PROBE_DIV && !b)) return fail(DIT_ERR_INVALID, "NULL pointer");
   if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
   return hip_status(dit::launch_probe_f32(op, out, a, b, n, mode, stream));
+}
+
+dit_status_t dit_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale,
+                           hipStream_t stream) {
+  if (op != DIT_PROBE_E4M3 && op != DIT_PROBE_FP8_QUANT) return fail(DIT_ERR_INVALID, "bad op");
+  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
+  if (n == 0) return DIT_OK;
+  if (!out || !in || (op == DIT_PROBE_FP8_QUANT && !scale))
+    return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
+  return hip_status(dit::launch_probe_fp8(op, out, in, n, scale, stream));
 }
 
 dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,

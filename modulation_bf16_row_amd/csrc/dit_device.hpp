@@ -266,6 +266,39 @@ __device__ __forceinline__ void store8(uint16_t *p, const V8 &v) {
 #endif
 }
 
+// Eight bytes (two words) with a nontemporal store.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8b(uint8_t *p, uint32_t w0, uint32_t w1) {
+  const u32x2 u = {w0, w1};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x2 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// OCP E4M3 codes of two binary32 values: saturated to +-448 (the largest
+// finite E4M3 value), then converted by v_cvt_pk_fp8_f32 (round to nearest
+// even, OCP format on gfx950); NaN passes the clamp unchanged and stays NaN.
+// Returns the codes of a and b in bits 0-7 and 8-15.  The device test checks
+// it against the oracle's encoder on every binary32 input between 2^-11 and
+// 2^10 in magnitude and on the edges outside.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sat448(float v) {
+  return v == v ? fminf(fmaxf(v, -448.0f), 448.0f) : v;
+}
+
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false) & 0xFFFFu;
+}
+
+// E4M3 codes of the eight bf16 values of v divided by s (IEEE division), as
+// two words (codes of elements 0-3, 4-7).
+__device__ __forceinline__ void quant8(const uint32_t (&w)[4], float s, uint32_t &q0,
+                                       uint32_t &q1) {
+  q0 = e4m3x2(__uint_as_float(w[0] << 16) / s, __uint_as_float(w[0] & 0xFFFF0000u) / s) |
+       (e4m3x2(__uint_as_float(w[1] << 16) / s, __uint_as_float(w[1] & 0xFFFF0000u) / s) << 16);
+  q1 = e4m3x2(__uint_as_float(w[2] << 16) / s, __uint_as_float(w[2] & 0xFFFF0000u) / s) |
+       (e4m3x2(__uint_as_float(w[3] << 16) / s, __uint_as_float(w[3] & 0xFFFF0000u) / s) << 16);
+}
+
 __device__ __forceinline__ float elem(const V8 &v, int j) {
   return (j & 1) ? hi(v.w[j >> 1]) : lo(v.w[j >> 1]);
 }

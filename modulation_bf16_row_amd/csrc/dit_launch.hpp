@@ -32,6 +32,10 @@ struct LnModArgs {
   float eps;
   int64_t rows_per_wave;       // set by the launcher
   int64_t blocks_per_mod;      // set by the launcher (staged layout)
+  // BF16 + E4M3 dual output (null out8: BF16 only)
+  uint8_t *out8;
+  int64_t out8_rs;
+  const float *fp8_scale;
 };
 
 struct GateLnArgs {
@@ -42,6 +46,10 @@ struct GateLnArgs {
   float eps;
   int64_t rows_per_wave;       // set by the launcher
   int64_t blocks_per_mod;      // set by the launcher (staged layout)
+  // BF16 + E4M3 dual output (null out8: BF16 only)
+  uint8_t *out8;
+  int64_t out8_rs;
+  const float *fp8_scale;
 };
 
 struct RmsScaleArgs {
@@ -107,5 +115,7 @@ hipError_t launch_probe_f32(int op, float *out, const float *a, const float *b, 
 hipError_t launch_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
                                 hipStream_t s);
 hipError_t launch_probe_copy(void *out, const void *in, int64_t n16, int flags, hipStream_t s);
+hipError_t launch_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale,
+                            hipStream_t s);
 
 }  // namespace dit

@@ -123,6 +123,26 @@ hipError_t launch_probe_copy(void *out, const void *in, int64_t n16, int flags, 
   return hipGetLastError();
 }
 
+// op 0: E4M3 code of the binary32 in[i]; op 1: E4M3 code of the bf16 in[i]
+// divided by *scale -- the quantization of the dual-output producers.
+__global__ void k_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v;
+  if (op == 0) {
+    v = static_cast<const float *>(in)[i];
+  } else {
+    v = __uint_as_float((uint32_t) static_cast<const uint16_t *>(in)[i] << 16) / *scale;
+  }
+  out[i] = (uint8_t)(e4m3x2(v, 0.0f) & 0xFFu);
+}
+
+hipError_t launch_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale,
+                            hipStream_t s) {
+  DIT_LAUNCH(k_probe_fp8, flat_grid(n, 256), dim3(256), 0, s, op, out, in, n, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t s) {
   DIT_LAUNCH(k_probe_bf16_round, flat_grid(n, 256), dim3(256), 0, s, out, in, n);
   return hipGetLastError();

@@ -205,10 +205,11 @@ __device__ __forceinline__ void one_plus8(const V8 &s, float (&f)[8]) {
 }
 
 // out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) gives chunk c's
-// bf(1 + scale) and shift as binary32 values.
-template <int NC, class Mod>
-__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, const float (&d)[NC][8],
-                                                float rho, int lane, int dim, Mod mod) {
+// bf(1 + scale) and shift as binary32 values.  F8: also qrow = E4M3(out / qs).
+template <int NC, bool F8, class Mod>
+__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, uint8_t *qrow, float qs,
+                                                const float (&d)[NC][8], float rho, int lane,
+                                                int dim, Mod mod) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (!valid<NC>(c, lane, dim)) continue;
@@ -224,21 +225,27 @@ __device__ __forceinline__ void ln_modulate_out(uint16_t *orow, const float (&d)
       o.w[k] = pack(p0 + sh[2 * k], p1 + sh[2 * k + 1]);        // + shift
     }
     store8(orow + 512 * c + 8 * lane, o);
+    if (F8) {
+      uint32_t q0, q1;
+      quant8(o.w, qs, q0, q1);
+      store8b(qrow + 512 * c + 8 * lane, q0, q1);
+    }
   }
 }
 
 
 // ---------------------------------------------------------------------------
-// LayerNorm + AdaLN modulate
+// LayerNorm + AdaLN modulate; F8: also the E4M3 copy out8 = E4M3(out / s).
 // LDS (staged): [0] = bf(1 + scale), [1] = shift, binary32.
 // ---------------------------------------------------------------------------
-template <int NC, int MODE, bool STAGED>
+template <int NC, int MODE, bool STAGED, bool F8>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(LnModArgs a) {
   extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   constexpr int kRow = stage_vecs<NC>();
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
+  const float qs = F8 ? *a.fp8_scale : 1.0f;
   if (STAGED) {
     for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
       float s1[8], sh[8];
@@ -261,17 +268,20 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(L
     float d[NC][8];
     const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
     uint16_t *orow = a.out + r * a.out_rs;
+    uint8_t *qrow = F8 ? a.out8 + r * a.out8_rs : nullptr;
     if (STAGED) {
       phase_barrier();
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
-        stage_get(lds, c, lane, s1);
-        stage_get(lds + kRow, c, lane, sh);
-      });
+      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+                              [&](int c, float (&s1)[8], float (&sh)[8]) {
+                                stage_get(lds, c, lane, s1);
+                                stage_get(lds + kRow, c, lane, sh);
+                              });
     } else {
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
-        one_plus8(sc[c], s1);
-        unpack8(sf[c], sh);
-      });
+      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+                              [&](int c, float (&s1)[8], float (&sh)[8]) {
+                                one_plus8(sc[c], s1);
+                                unpack8(sf[c], sh);
+                              });
     }
   }
 }
@@ -280,9 +290,10 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(L
 // Gated residual + LayerNorm + AdaLN modulate: r' = bf(residual + bf(gate * y))
 // is written to out_res, and LN + modulate of r' to out.  The row is read
 // once; r' never goes back through HBM before the LayerNorm.
+// F8: also the E4M3 copy out8 = E4M3(out / s).
 // LDS (staged): [0] = gate, [1] = bf(1 + scale), [2] = shift, binary32.
 // ---------------------------------------------------------------------------
-template <int NC, int MODE, bool STAGED>
+template <int NC, int MODE, bool STAGED, bool F8>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_modulate(
     GateLnArgs a) {
   extern __shared__ float4 lds[];
@@ -290,6 +301,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_m
   constexpr int kRow = stage_vecs<NC>();
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
+  const float qs = F8 ? *a.fp8_scale : 1.0f;
   if (STAGED) {
     for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
       const int64_t off = sp.m * a.mod_rs + 8 * v;
@@ -341,17 +353,20 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_m
     float d[NC][8];
     const float rho = ln_stats<NC, MODE>(xv, d, lane, dim, a.eps);
     uint16_t *orow = a.out + r * a.out_rs;
+    uint8_t *qrow = F8 ? a.out8 + r * a.out8_rs : nullptr;
     if (STAGED) {
       phase_barrier();
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
-        stage_get(lds + kRow, c, lane, s1);
-        stage_get(lds + 2 * kRow, c, lane, sh);
-      });
+      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+                              [&](int c, float (&s1)[8], float (&sh)[8]) {
+                                stage_get(lds + kRow, c, lane, s1);
+                                stage_get(lds + 2 * kRow, c, lane, sh);
+                              });
     } else {
-      ln_modulate_out<NC>(orow, d, rho, lane, dim, [&](int c, float (&s1)[8], float (&sh)[8]) {
-        one_plus8(sc[c], s1);
-        unpack8(sf[c], sh);
-      });
+      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+                              [&](int c, float (&s1)[8], float (&sh)[8]) {
+                                one_plus8(sc[c], s1);
+                                unpack8(sf[c], sh);
+                              });
     }
   }
 }
@@ -626,29 +641,29 @@ static Shape row_shape(int64_t rows, int64_t per_mod, int64_t dim, int staged_ro
   else                                                              \
     DIT_LAUNCH(KF, sh.grid, dim3(kThreads), shm_f, s, a);
 
-template <int MODE>
+template <int MODE, bool F8>
 static hipError_t ln_dispatch(LnModArgs a, hipStream_t s) {
   const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 2);
   a.rows_per_wave = sh.rows_per_wave;
   a.blocks_per_mod = sh.blocks_per_mod;
 #define X(N)                                                                              \
   case N:                                                                                 \
-    DIT_ROW_LAUNCH((k_ln_modulate<N, MODE, true>), (k_ln_modulate<N, MODE, false>),       \
+    DIT_ROW_LAUNCH((k_ln_modulate<N, MODE, true, F8>), (k_ln_modulate<N, MODE, false, F8>), \
                    stage_bytes(a.dim, 2), 0);                                             \
     break;
   DIT_ROW_DISPATCH();
 #undef X
 }
 
-template <int MODE>
+template <int MODE, bool F8>
 static hipError_t gate_ln_dispatch(GateLnArgs a, hipStream_t s) {
   const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 3);
   a.rows_per_wave = sh.rows_per_wave;
   a.blocks_per_mod = sh.blocks_per_mod;
 #define X(N)                                                                     \
   case N:                                                                        \
-    DIT_ROW_LAUNCH((k_gate_add_ln_modulate<N, MODE, true>),                      \
-                   (k_gate_add_ln_modulate<N, MODE, false>), stage_bytes(a.dim, 3), 0); \
+    DIT_ROW_LAUNCH((k_gate_add_ln_modulate<N, MODE, true, F8>),                  \
+                   (k_gate_add_ln_modulate<N, MODE, false, F8>), stage_bytes(a.dim, 3), 0); \
     break;
   DIT_ROW_DISPATCH();
 #undef X
@@ -698,11 +713,17 @@ static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
 }
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s) {
-  return mode == kFast ? ln_dispatch<kFast>(a, s) : ln_dispatch<kLossless>(a, s);
+  if (a.out8)
+    return mode == kFast ? ln_dispatch<kFast, true>(a, s) : ln_dispatch<kLossless, true>(a, s);
+  return mode == kFast ? ln_dispatch<kFast, false>(a, s) : ln_dispatch<kLossless, false>(a, s);
 }
 
 hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t s) {
-  return mode == kFast ? gate_ln_dispatch<kFast>(a, s) : gate_ln_dispatch<kLossless>(a, s);
+  if (a.out8)
+    return mode == kFast ? gate_ln_dispatch<kFast, true>(a, s)
+                         : gate_ln_dispatch<kLossless, true>(a, s);
+  return mode == kFast ? gate_ln_dispatch<kFast, false>(a, s)
+                       : gate_ln_dispatch<kLossless, false>(a, s);
 }
 
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s) {

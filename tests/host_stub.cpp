@@ -24,15 +24,16 @@ static void rec(const char *name, int mode, const int64_t *v, int n) {
 namespace dit {
 
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t) {
-  const int64_t v[] = {a.rows, a.dim, a.per_mod, a.out_rs, a.x_rs, a.mod_rs};
-  rec("ln_modulate", mode, v, 6);
+  const int64_t v[] = {a.rows, a.dim, a.per_mod, a.out_rs, a.x_rs, a.mod_rs, a.out8 != nullptr,
+                       a.out8_rs};
+  rec(a.out8 ? "ln_modulate_fp8" : "ln_modulate", mode, v, 8);
   return hipSuccess;
 }
 
 hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t) {
-  const int64_t v[] = {a.rows,   a.dim,  a.per_mod, a.out_res_rs, a.out_rs,
-                       a.res_rs, a.y_rs, a.mod_rs};
-  rec("gate_add_ln_modulate", mode, v, 8);
+  const int64_t v[] = {a.rows,   a.dim,  a.per_mod, a.out_res_rs,        a.out_rs,
+                       a.res_rs, a.y_rs, a.mod_rs,  a.out8 != nullptr, a.out8_rs};
+  rec(a.out8 ? "gate_add_ln_modulate_fp8" : "gate_add_ln_modulate", mode, v, 10);
   return hipSuccess;
 }
 
@@ -58,6 +59,12 @@ hipError_t launch_qk_norm_rope(const QkvArgs &a, int mode, hipStream_t) {
   const int64_t v[] = {a.batch, a.heads, a.s_total, a.out_ts, a.out_bs, a.txt.tokens,
                        a.img.tokens, a.txt.tok_stride, a.img.tok_stride};
   rec("qk_norm_rope", mode, v, 9);
+  return hipSuccess;
+}
+
+hipError_t launch_probe_fp8(int op, uint8_t *, const void *, int64_t n, const float *,
+                            hipStream_t) {
+  rec("probe_fp8", op, &n, 1);
   return hipSuccess;
 }
 

@@ -64,6 +64,11 @@ def stub(tmp_path_factory):
                                           vp]
     lib.dit_gate_add_ln_modulate.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64,
                                              i64, i64, i64, f32, cint, vp]
+    lib.dit_ln_modulate_fp8.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64,
+                                        f32, vp, cint, vp]
+    lib.dit_gate_add_ln_modulate_fp8.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
+                                                 vp, vp, i64, i64, i64, i64, f32, vp, cint, vp]
+    lib.dit_probe_fp8.argtypes = [cint, vp, vp, i64, vp, vp]
     return lib
 
 
@@ -198,6 +203,56 @@ def test_gate_add_ln_rejections_touch_nothing(stub, kw, status, why):
     assert gate_ln(stub, **kw) == status
     assert r.calls == n0, "a rejected call must not launch"
     assert why.lower() in stub.dit_status_reason().decode().lower()
+
+
+Q8, FS = A * 11, A * 12          # E4M3 output and the fp8 scale
+
+
+def ln8(lib, q8=Q8, q8_rs=512, fs=FS, out=OUT, x=X, rows=8, dim=512, mode=0):
+    return lib.dit_ln_modulate_fp8(out, 512, q8, q8_rs, x, 512, SC, SH, 512, 1, rows, dim, 1e-6,
+                                   fs, mode, None)
+
+
+def test_ln_modulate_fp8_guards(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert ln8(stub, q8_rs=1024) == OK
+    assert r.calls == n0 + 1 and r.name == "ln_modulate_fp8"
+    assert r.vals[6:8] == [1, 1024]
+    for kw, status, why in [
+            (dict(q8=0), INVALID, "out_fp8 is NULL"),
+            (dict(fs=0), INVALID, "fp8_scale is NULL"),
+            (dict(q8_rs=500), UNSUPPORTED, "out_fp8 row stride"),
+            (dict(q8_rs=516), UNSUPPORTED, "out_fp8 row stride"),
+            (dict(q8=Q8 + 4), UNSUPPORTED, "8-byte"),
+            (dict(fs=FS + 2), UNSUPPORTED, "4-byte"),
+            (dict(q8=X), INVALID, "overlaps"),                 # writes the input
+            (dict(q8=OUT + 512), INVALID, "overlaps"),         # inside the bf16 output
+            (dict(q8=FS - 1024, q8_rs=512), INVALID, "fp8_scale"),
+            (dict(fs=OUT + 64), INVALID, "fp8_scale")]:
+        n0 = r.calls
+        assert ln8(stub, **kw) == status, kw
+        assert r.calls == n0
+        assert why.lower() in stub.dit_status_reason().decode().lower(), (kw, why)
+
+
+def test_gate_add_ln_modulate_fp8_guards(stub):
+    r = Rec(stub)
+    f = stub.dit_gate_add_ln_modulate_fp8
+    assert f(OUT, 512, A * 10, 512, Q8, 512, RES, 512, Y, 512, G, SC, SH, 512, 2, 8, 512, 1e-6, FS,
+             1, None) == OK
+    assert r.name == "gate_add_ln_modulate_fp8" and r.vals[8:10] == [1, 512]
+    assert f(OUT, 512, A * 10, 512, RES, 512, RES, 512, Y, 512, G, SC, SH, 512, 2, 8, 512, 1e-6,
+             FS, 0, None) == INVALID                                  # E4M3 over the residual
+    assert f(OUT, 512, A * 10, 512, Q8, 512, RES, 512, Y, 512, G, SC, SH, 512, 2, 8, 512, 1e-6,
+             OUT, 0, None) == INVALID                                 # scale inside an output
+
+
+def test_probe_fp8_guards(stub):
+    assert stub.dit_probe_fp8(2, Q8, X, 16, None, None) == INVALID
+    assert stub.dit_probe_fp8(1, Q8, X, 16, None, None) == INVALID    # quant needs the scale
+    assert stub.dit_probe_fp8(0, Q8, X, 16, None, None) == OK
+    assert stub.dit_probe_fp8(0, Q8, X, 0, None, None) == OK
 
 
 class Stream(ctypes.Structure):

@@ -1,4 +1,5 @@
-"""LOSSLESS parity of the fused producers with the CPU oracle, bit for bit.
+"""LOSSLESS parity of the fused producers with the CPU oracle, bit for bit
+(E4M3 outputs code for code).
 
 Gated residual + LayerNorm/AdaLN (page "基于Agent的SGLang扩散模型Kernel优化实践",
 sections "将FP8量化融合到前序算子" and "NVFP4的三组优化"): r' = bf(residual +
@@ -13,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from exact import value_of_bf16
 from gpu_util import assert_bits_equal, dev, host, say
 from modulation_bf16_row_amd import synth
 
@@ -112,3 +114,142 @@ def test_gate_add_ln_qwen_block_full_size():
                                                   w["shift"], w["eps"])
     assert_bits_equal(host(rp), ref_rp, "qwen r'")
     assert_bits_equal(host(out), ref_out, "qwen out")
+
+
+# --------------------------------------------------------------------------------------
+# BF16 + static E4M3 dual output (page "基于Agent的SGLang扩散模型Kernel优化实践", section
+# "将FP8量化融合到前序算子")
+# --------------------------------------------------------------------------------------
+
+def _e4m3_equal(got, ref, what):
+    """Code equality; NaN codes (0x7F / 0xFF) compare as NaN on both sides."""
+    got, ref = np.asarray(got, dtype=np.uint8), np.asarray(ref, dtype=np.uint8)
+    gn, rn = (got & 0x7F) == 0x7F, (ref & 0x7F) == 0x7F
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+    bad = np.flatnonzero((got != ref) & ~gn)
+    assert bad.size == 0, (f"{what}: {bad.size} codes differ, first "
+                           f"got={[hex(int(v)) for v in got[bad[:6]]]} "
+                           f"ref={[hex(int(v)) for v in ref[bad[:6]]]}")
+
+
+def test_e4m3_conversion_every_input_in_range():
+    """The kernels' conversion against the oracle on every positive binary32
+    value in [2^-11, 2^10) (zero codes below, saturation above), a sample of
+    negatives, and the edges outside the range."""
+    say("e4m3 conversion, every positive binary32 in [2^-11, 2^10)")
+    first, last = 0x3A000000, 0x44800000
+    chunk = 1 << 24
+    for start in range(first, last, chunk):
+        n = min(chunk, last - start)
+        bits = torch.arange(start, start + n, dtype=torch.int32, device="cuda")
+        got = m().dit_probe_fp8(0, bits.view(torch.float32)).cpu().numpy()
+        _e4m3_equal(got, oracle.e4m3_bits_range(start, n), hex(start))
+        del bits
+    say("e4m3 conversion, negatives and edges")
+    rng = np.random.default_rng(130)
+    neg = (rng.integers(first, last, 1 << 20, dtype=np.uint64) | 0x80000000).astype(np.uint32)
+    edges = []
+    for e in range(256):
+        for mant in (0, 1, 0x400000, 0x7FFFFF):
+            edges += [(e << 23) | mant, 0x80000000 | (e << 23) | mant]
+    bits = np.concatenate([neg, np.array(edges, dtype=np.uint32)])
+    got = m().dit_probe_fp8(0, torch.from_numpy(bits.view(np.float32)).cuda()).cpu().numpy()
+    _e4m3_equal(got, oracle.e4m3(bits.view(np.float32)), "negatives and edges")
+
+
+@pytest.mark.parametrize("fp8_scale", [1.0, 3.1, 0.3, 0.0173, 2.0 ** -3, 179.2])
+def test_fp8_quantization_every_bf16(fp8_scale):
+    """E4M3(h / s) for every bf16 h: the kernels' division and conversion
+    against an IEEE binary32 division and the oracle's encoder."""
+    say("fp8 quantization, every bf16, scale", fp8_scale)
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = torch.tensor([fp8_scale], dtype=torch.float32, device="cuda")
+    got = m().dit_probe_fp8(1, dev(codes), s).cpu().numpy()
+    with np.errstate(all="ignore"):
+        q = (value_of_bf16(codes).astype(np.float32) / np.float32(fp8_scale)).astype(np.float32)
+    _e4m3_equal(got, oracle.e4m3(q), f"scale {fp8_scale}")
+
+
+def _fs(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def _u8(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+@pytest.mark.parametrize("dim", [8, 520, 3072, 5120, 8192])
+@pytest.mark.parametrize("rows,mod_rows", [(1, 1), (37, 1), (36, 3), (37, 37)])
+def test_ln_modulate_fp8_shapes(dim, rows, mod_rows):
+    say("ln_modulate_fp8", dim, rows, mod_rows)
+    inp = _inputs(30 * dim + rows, rows, dim, mod_rows)
+    x, sc, sh = dev(inp["res"]), dev(inp["scale"]), dev(inp["shift"])
+    out, q = m().dit_ln_modulate_fp8(x, sc, sh, _fs(0.0173), EPS)
+    ref, ref8 = oracle.ln_modulate_fp8(inp["res"], inp["scale"], inp["shift"], EPS, 0.0173)
+    assert_bits_equal(host(out), ref, f"bf16 dim={dim} rows={rows}/{mod_rows}")
+    _e4m3_equal(_u8(q), ref8, f"e4m3 dim={dim} rows={rows}/{mod_rows}")
+
+
+@pytest.mark.parametrize("dim,rows,mod_rows", [(520, 37, 1), (3072, 64, 2), (5120, 12, 12),
+                                              (8192, 8, 2)])
+def test_gate_add_ln_modulate_fp8_shapes(dim, rows, mod_rows):
+    say("gate_add_ln_modulate_fp8", dim, rows, mod_rows)
+    inp = _inputs(40 * dim + rows, rows, dim, mod_rows)
+    rp, out, q = m().dit_gate_add_ln_modulate_fp8(*_dev_all(inp), _fs(3.1), EPS)
+    refs = oracle.gate_add_ln_modulate_fp8(inp["res"], inp["y"], inp["gate"], inp["scale"],
+                                           inp["shift"], EPS, 3.1)
+    assert_bits_equal(host(rp), refs[0], "r'")
+    assert_bits_equal(host(out), refs[1], "out")
+    _e4m3_equal(_u8(q), refs[2], "e4m3")
+
+
+@pytest.mark.parametrize("mode", ["lossless", "fast"])
+def test_fp8_bf16_outputs_equal_bf16_only_calls(mode):
+    say("fp8 producers: bf16 outputs vs bf16-only calls", mode)
+    inp = _inputs(555, 96, 3072, 2)
+    res, y, g, sc, sh = _dev_all(inp)
+    out, q = m().dit_ln_modulate_fp8(res, sc, sh, _fs(0.05), EPS, mode)
+    assert_bits_equal(host(out), host(m().dit_ln_modulate(res, sc, sh, EPS, mode)), "ln")
+    rp, out2, q2 = m().dit_gate_add_ln_modulate_fp8(res, y, g, sc, sh, _fs(0.05), EPS, mode)
+    rp_ref, out_ref = m().dit_gate_add_ln_modulate(res, y, g, sc, sh, EPS, mode)
+    assert_bits_equal(host(rp), host(rp_ref), "r'")
+    assert_bits_equal(host(out2), host(out_ref), "gated out")
+    # the E4M3 copy is the quantization of the BF16 output, in both modes
+    ref8 = m().dit_probe_fp8(1, out2, _fs(0.05)).cpu().numpy()
+    _e4m3_equal(_u8(q2), ref8, "e4m3 of out")
+
+
+def test_fp8_in_place_and_uint8_output():
+    say("fp8 producers in place")
+    rows, dim = 24, 1032
+    inp = _inputs(556, rows, dim, 2)
+    refs = oracle.gate_add_ln_modulate_fp8(inp["res"], inp["y"], inp["gate"], inp["scale"],
+                                           inp["shift"], EPS, 0.3)
+    res, y, g, sc, sh = _dev_all(inp)
+    q = torch.empty((rows, dim), dtype=torch.uint8, device="cuda")
+    m().dit_gate_add_ln_modulate_fp8(res, y, g, sc, sh, _fs(0.3), EPS, out_residual=res, out=y,
+                                     out_fp8=q)
+    assert_bits_equal(host(res), refs[0], "r' in residual")
+    assert_bits_equal(host(y), refs[1], "out in y")
+    _e4m3_equal(q.cpu().numpy(), refs[2], "e4m3 uint8")
+
+
+def test_fp8_qwen_block_full_size():
+    """The Qwen-Image 1024x1024 block [9216, 3072]: both dual-output
+    producers, every element of every output."""
+    w = synth.qwen_image_block()
+    say("ln_modulate_fp8 qwen block [9216,3072]")
+    out, q = m().dit_ln_modulate_fp8(dev(w["x"]), dev(w["scale"]), dev(w["shift"]), _fs(0.0173),
+                                     w["eps"])
+    ref, ref8 = oracle.ln_modulate_fp8(w["x"], w["scale"], w["shift"], w["eps"], 0.0173)
+    assert_bits_equal(host(out), ref, "qwen ln bf16")
+    _e4m3_equal(_u8(q), ref8, "qwen ln e4m3")
+    say("gate_add_ln_modulate_fp8 qwen block")
+    rp, out, q = m().dit_gate_add_ln_modulate_fp8(
+        dev(w["residual"]), dev(w["x"]), dev(w["gate"]), dev(w["scale"]), dev(w["shift"]),
+        _fs(0.0173), w["eps"])
+    refs = oracle.gate_add_ln_modulate_fp8(w["residual"], w["x"], w["gate"], w["scale"],
+                                           w["shift"], w["eps"], 0.0173)
+    assert_bits_equal(host(rp), refs[0], "qwen r'")
+    assert_bits_equal(host(out), refs[1], "qwen out")
+    _e4m3_equal(_u8(q), refs[2], "qwen e4m3")
