@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 
-SOURCES = ["dit_rows.hip", "dit_qkv.hip", "dit_probe.hip", "dit_abi.cpp"]
+SOURCES = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_qkv.hip",
+           "dit_probe.hip", "dit_abi.cpp"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -59,7 +60,7 @@ def _compile(src, verbose, build_dir, extra):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 4, lib: str = LIB, extra_flags=()) -> str:
+def build(verbose: bool = False, jobs: int = 7, lib: str = LIB, extra_flags=()) -> str:
     """Compiles and links the library; `lib` and `extra_flags` allow side
     builds (e.g. with -D macros) without touching the default one."""
     build_dir = BUILD if lib == LIB else os.path.join(BUILD, os.path.basename(lib) + ".d")

@@ -1,0 +1,82 @@
+// dit_ln.hpp -- LayerNorm + AdaLN modulate helpers shared by the LN kernel
+// (dit_ln.hip) and the gated residual + LayerNorm/AdaLN producer
+// (dit_gate_ln.hip): two-pass statistics and the modulated output, with an
+// optional E4M3 copy.
+#pragma once
+
+#include "dit_rows.hpp"
+
+namespace dit {
+
+// ---------------------------------------------------------------------------
+// LayerNorm + AdaLN modulate, as helpers on a row held by the wave.
+// ---------------------------------------------------------------------------
+// Two-pass statistics in order R: returns rho = 1 / sqrt(var + eps) and
+// leaves the deviations x - mean (binary32) in d.
+template <int NC, int MODE>
+__device__ __forceinline__ float ln_stats(const V8 (&xv)[NC], float (&d)[NC][8], int lane,
+                                          int dim, float eps) {
+  float p = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (valid<NC>(c, lane, dim))
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p = p + elem(xv[c], j);
+  const float mean = wave_sum(p) / (float)dim;
+
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (valid<NC>(c, lane, dim))
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        d[c][j] = elem(xv[c], j) - mean;
+        if (MODE == kLossless)
+          q = q + d[c][j] * d[c][j];
+        else
+          q = fmaf(d[c][j], d[c][j], q);
+      }
+  const float var = wave_sum(q) / (float)dim;
+  return rsqrt_mode<MODE>(var + eps);
+}
+
+// bf(1 + scale) of each of the 8 values.
+__device__ __forceinline__ void one_plus8(const V8 &s, float (&f)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = 1.0f + lo(s.w[k]);
+    f[2 * k + 1] = 1.0f + hi(s.w[k]);
+    round2(f[2 * k], f[2 * k + 1]);
+  }
+}
+
+// out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) gives chunk c's
+// bf(1 + scale) and shift as binary32 values.  F8: also qrow = E4M3(out / qs).
+template <int NC, bool F8, class Mod>
+__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, uint8_t *qrow, float qs,
+                                                const float (&d)[NC][8], float rho, int lane,
+                                                int dim, Mod mod) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (!valid<NC>(c, lane, dim)) continue;
+    float s1[8], sh[8];
+    mod(c, s1, sh);
+    V8 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float n0 = d[c][2 * k] * rho, n1 = d[c][2 * k + 1] * rho;
+      round2(n0, n1);                                           // LayerNorm output
+      float p0 = n0 * s1[2 * k], p1 = n1 * s1[2 * k + 1];
+      round2(p0, p1);                                           // product
+      o.w[k] = pack(p0 + sh[2 * k], p1 + sh[2 * k + 1]);        // + shift
+    }
+    store8(orow + 512 * c + 8 * lane, o);
+    if (F8) {
+      uint32_t q0, q1;
+      quant8(o.w, qs, q0, q1);
+      store8b(qrow + 512 * c + 8 * lane, q0, q1);
+    }
+  }
+}
+
+}  // namespace dit

@@ -1,0 +1,196 @@
+// dit_rms.hip -- gfx950 native-bf16 RMSNorm-scale and RMSNorm-tanh-residual.
+// Geometry, staging and launch shapes: dit_rows.hpp.
+#include "dit_rows.hpp"
+
+namespace dit {
+
+// ---------------------------------------------------------------------------
+// Native-bf16 RMSNorm: the chain's bf16 rstd of one row.
+// ---------------------------------------------------------------------------
+template <int NC, int MODE>
+__device__ __forceinline__ float rms_rstd(const V8 (&xv)[NC], int lane, int dim, float eps) {
+  float p = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (valid<NC>(c, lane, dim))
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float t0 = lo(xv[c].w[k]), t1 = hi(xv[c].w[k]);
+        t0 = t0 * t0;
+        t1 = t1 * t1;
+        round2(t0, t1);                                  // bf16 squares
+        p = p + t0;
+        p = p + t1;
+      }
+  const float ms = round1(wave_sum(p) / (float)dim);     // bf16 mean square
+  const float v = round1(ms + eps);                      // bf16 (ms + eps)
+  return round1(rsqrt_mode<MODE>(v));                    // bf16 rstd
+}
+
+// y2 = bf(bf(x * rstd) * w) for the pair in word xw (weights w0, w1).
+__device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, float w0, float w1,
+                                       float rstd) {
+  y0 = lo(xw) * rstd;
+  y1 = hi(xw) * rstd;
+  round2(y0, y1);
+  y0 = y0 * w0;
+  y1 = y1 * w1;
+  round2(y0, y1);
+}
+
+// The RMSNorm weight as a staged row (every launch, both layouts).
+__device__ __forceinline__ void stage_weight(float4 *row, const uint16_t *weight, int dim) {
+  for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+    float w[8];
+    unpack8(load8(weight + 8 * v), w);
+    stage_put(row, v, w);
+  }
+}
+
+// LDS: [0] = weight (always), [1] = scale (staged), binary32.
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale(RmsScaleArgs a) {
+  extern __shared__ float4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  constexpr int kRow = stage_vecs<NC>();
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
+  if (sp.wg_empty) return;                                 // whole workgroup idle
+  stage_weight(lds, a.weight, dim);
+  if (STAGED) {
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      float s[8];
+      unpack8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s);
+      stage_put(lds + kRow, v, s);
+    }
+  }
+  __syncthreads();
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 xv[NC], sc[NC];
+    load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
+    if (!STAGED) load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
+    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+    phase_barrier();
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      float w[8], s[8];
+      stage_get(lds, c, lane, w);
+      if (STAGED)
+        stage_get(lds + kRow, c, lane, s);
+      else
+        unpack8(sc[c], s);
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float y0, y1;
+        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
+        o.w[k] = pack(y0 * s[2 * k], y1 * s[2 * k + 1]);
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
+  }
+}
+
+// LDS: [0] = weight (always), [1] = tanh(gate) (staged), binary32; then the
+// tanh table.  tanh comes from the table in both modes.
+template <int NC, int MODE, bool STAGED>
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_residual(
+    RmsTanhArgs a) {
+  extern __shared__ float4 lds[];
+  const int lane = threadIdx.x & 63, dim = (int)a.dim;
+  constexpr int kRow = stage_vecs<NC>();
+  uint16_t *tab = reinterpret_cast<uint16_t *>(lds + (STAGED ? 2 : 1) * kRow);
+  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+                         : spans(a.rows, a.rows_per_wave);
+  if (sp.wg_empty) return;                                 // whole workgroup idle
+  tanh_table_fill(tab, threadIdx.x, kThreads);
+  stage_weight(lds, a.weight, dim);
+  __syncthreads();
+  if (STAGED) {
+    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+      const V8 g = load8(a.gate + sp.m * a.mod_rs + 8 * v);
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = tanh_lookup(elem(g, j), tab);
+      stage_put(lds + kRow, v, t);
+    }
+    __syncthreads();
+  }
+
+  for (int64_t r = sp.begin; r < sp.end; ++r) {
+    V8 xv[NC], rv[NC], tau[NC];
+    load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
+    const int64_t m = STAGED ? sp.m : r / a.per_mod;
+    if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
+    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+    phase_barrier();
+    uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!valid<NC>(c, lane, dim)) continue;
+      float w[8], tg[8];
+      stage_get(lds, c, lane, w);
+      if (STAGED) {
+        stage_get(lds + kRow, c, lane, tg);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tg[j] = tanh_lookup(elem(tau[c], j), tab);
+      }
+      V8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float y0, y1;
+        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
+        float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
+        round2(q0, q1);                                   // bf(tanh(gate) * y2)
+        o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
+      }
+      store8(orow + 512 * c + 8 * lane, o);
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t rms_scale_dispatch(RmsScaleArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 2);
+  a.rows_per_wave = sh.rows_per_wave;
+  a.blocks_per_mod = sh.blocks_per_mod;
+#define X(N)                                                                              \
+  case N:                                                                                 \
+    DIT_ROW_LAUNCH((k_rmsnorm_scale<N, MODE, true>), (k_rmsnorm_scale<N, MODE, false>),   \
+                   stage_bytes(a.dim, 2), stage_bytes(a.dim, 1));                         \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
+}
+
+template <int MODE>
+static hipError_t rms_tanh_dispatch(RmsTanhArgs a, hipStream_t s) {
+  const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 2);
+  a.rows_per_wave = sh.rows_per_wave;
+  a.blocks_per_mod = sh.blocks_per_mod;
+  const size_t tab = kTanhTabVecs * sizeof(uint4);
+#define X(N)                                                                          \
+  case N:                                                                             \
+    DIT_ROW_LAUNCH((k_rmsnorm_tanh_residual<N, MODE, true>),                          \
+                   (k_rmsnorm_tanh_residual<N, MODE, false>),                         \
+                   stage_bytes(a.dim, 2) + tab, stage_bytes(a.dim, 1) + tab);         \
+    break;
+  DIT_ROW_DISPATCH();
+#undef X
+}
+
+hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s) {
+  return mode == kFast ? rms_scale_dispatch<kFast>(a, s) : rms_scale_dispatch<kLossless>(a, s);
+}
+
+hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStream_t s) {
+  return mode == kFast ? rms_tanh_dispatch<kFast>(a, s) : rms_tanh_dispatch<kLossless>(a, s);
+}
+
+}  // namespace dit

@@ -78,6 +78,8 @@ def load(path=None):
     lib.orc_gate_add_ln_modulate.argtypes = [_u16p, _i64, _u16p, _i64, _u16p, _i64, _u16p, _i64,
                                              _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
                                              ctypes.c_float]
+    lib.orc_wan_mod_table.restype = ctypes.c_int
+    lib.orc_wan_mod_table.argtypes = [_f32p, _f32p, _u16p, _i64, _i64, _i64, _i64]
     lib.orc_qk_norm_rope.restype = ctypes.c_int
     lib.orc_qk_norm_rope.argtypes = [_u16p, _u16p, _u16p, _i64, _i64,
                                      ctypes.POINTER(QkvStream), ctypes.POINTER(QkvStream),
@@ -370,6 +372,18 @@ def gate_add_ln_modulate_fp8(residual, y, gate, scale, shift, eps=1e-6, fp8_scal
         _p16(gate), _p16(scale), _p16(shift), m_rs, gate.shape[0], rows, dim,
         ctypes.c_float(eps), ctypes.c_float(fp8_scale)))
     return out_res, out, out8
+
+
+def wan_mod_table(table, temb):
+    """table: float32 [n_mod, D]; temb: bf16 bits [B, S, n_mod, D].  Returns
+    float32 [n_mod, B, S, D] = table[k] + temb[:, :, k] (binary32)."""
+    table = np.ascontiguousarray(table, dtype=np.float32)
+    temb = np.ascontiguousarray(temb, dtype=np.uint16)
+    B, S, K, D = temb.shape
+    assert table.shape == (K, D)
+    out = np.empty((K, B, S, D), dtype=np.float32)
+    _check(load().orc_wan_mod_table(_p32(out), _p32(table), _p16(temb), B, S, K, D))
+    return out
 
 
 def _stream(q, k, v, qw, kw):

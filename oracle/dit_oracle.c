@@ -409,6 +409,28 @@ void orc_e4m3_bits_range(uint32_t first, int64_t n, uint8_t *out) {
 }
 
 /* ------------------------------------------------------------------------- */
+/* Wan per-token modulation table  [P1 Wan视频模型的数据搬运优化: the binary32    */
+/*  sum of the block's modulation table and the per-token time embedding,     */
+/*  written as n_mod contiguous [B, S, D] tensors instead of strided chunks]  */
+/* ------------------------------------------------------------------------- */
+
+/* out[k][b][s][i] = table[k][i] + temb[b][s][k][i] (one binary32 addition;
+ * temb is bf16).  table: [n_mod, D] float; temb: [B, S, n_mod, D] bf16;
+ * out: [n_mod, B, S, D] float, all contiguous. */
+int orc_wan_mod_table(float *out, const float *table, const uint16_t *temb, int64_t batch,
+                      int64_t tokens, int64_t n_mod, int64_t dim) {
+  if (batch < 0 || tokens < 0 || n_mod <= 0 || dim <= 0) return 1;
+  for (int64_t k = 0; k < n_mod; ++k)
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t s = 0; s < tokens; ++s)
+        for (int64_t i = 0; i < dim; ++i) {
+          const float e = orc_bf16_value(temb[((b * tokens + s) * n_mod + k) * dim + i]);
+          out[((k * batch + b) * tokens + s) * dim + i] = table[k * dim + i] + e;
+        }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Q/K RMSNorm + interleaved RoPE + joint QKV write                          */
 /* [P1 合并QKV投影时的数值问题: the four steps of the epilogue]                 */
 /* ------------------------------------------------------------------------- */

@@ -62,6 +62,8 @@ int orc_gate_add_ln_modulate_fp8(uint16_t *out_res, int64_t out_res_rs, uint16_t
                                  int64_t y_rs, const uint16_t *gate, const uint16_t *scale,
                                  const uint16_t *shift, int64_t mod_rs, int64_t mod_rows,
                                  int64_t rows, int64_t dim, float eps, float fp8_scale);
+int orc_wan_mod_table(float *out, const float *table, const uint16_t *temb, int64_t batch,
+                      int64_t tokens, int64_t n_mod, int64_t dim);
 void orc_e4m3_array(const float *in, uint8_t *out, int64_t n);
 void orc_e4m3_bits_range(uint32_t first, int64_t n, uint8_t *out);
 

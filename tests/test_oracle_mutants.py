@@ -87,6 +87,14 @@ MUTANTS = {
         "return orc_e4m3(orc_bf16_value(h) / scale);",
         "return orc_e4m3(orc_bf16_value(h) * (1.0f / scale));",
         ["test_fp8_quantization_divides_by_the_scale"]),
+    "modulation table written token-major": (
+        "out[((k * batch + b) * tokens + s) * dim + i] = table[k * dim + i] + e;",
+        "out[((b * tokens + s) * n_mod + k) * dim + i] = table[k * dim + i] + e;",
+        ["test_wan_mod_table_layout_with_tagged_values"]),
+    "modulation table reads chunk 0": (
+        "const float e = orc_bf16_value(temb[((b * tokens + s) * n_mod + k) * dim + i]);",
+        "const float e = orc_bf16_value(temb[((b * tokens + s) * n_mod) * dim + i]);",
+        ["test_wan_mod_table_layout_with_tagged_values"]),
     "RoPE sign": (
         "o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);",
         "o[2 * i] = orc_bf16_round(a * c[i] + b * z[i]);",

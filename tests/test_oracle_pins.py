@@ -693,6 +693,43 @@ def test_gate_add_ln_modulate_fp8():
 
 
 # --------------------------------------------------------------------------------------
+# Wan per-token modulation table (page "基于Agent的SGLang扩散模型Kernel优化实践", section
+# "Wan视频模型的数据搬运优化")
+# --------------------------------------------------------------------------------------
+
+def test_wan_mod_table_layout_with_tagged_values():
+    """table[k][i] = 4096 k and temb[b][s][k][i] = a small integer tag of
+    (b, s, k, i): every sum is exact, so each output element names the
+    operands that reached it; out is [n_mod, B, S, D]."""
+    B, S, K, D = 2, 5, 6, 24
+    table = np.repeat((4096.0 * np.arange(K, dtype=np.float32))[:, None], D, axis=1)
+    b, s_, k, i = np.meshgrid(np.arange(B), np.arange(S), np.arange(K), np.arange(D),
+                              indexing="ij")
+    tag = (b * 101 + s_ * 13 + k * 7 + i) % 250                    # exact in bf16
+    temb = nearest_bf16(tag.astype(np.float64)).reshape(B, S, K, D)
+    out = oracle.wan_mod_table(table, temb)
+    assert out.shape == (K, B, S, D)
+    for kk in range(K):
+        assert np.array_equal(out[kk], 4096.0 * kk + tag[:, :, kk, :].astype(np.float32))
+
+
+def test_wan_mod_table_one_rounding():
+    """Random fp32 table and bf16 time embedding: each output is the exact sum
+    rounded once to binary32 (the float64 sum is exact for these exponent
+    ranges, which the test checks)."""
+    rng = np.random.default_rng(140)
+    B, S, K, D = 1, 64, 6, 520
+    table = (rng.standard_normal((K, D)) * 0.05).astype(np.float32)
+    temb = nearest_bf16(rng.standard_normal((B, S, K, D)) * 0.3).reshape(B, S, K, D)
+    out = oracle.wan_mod_table(table, temb)
+    tv = value_of_bf16(temb)
+    exact = table[None, None].astype(np.float64) + tv            # [B, S, K, D]
+    assert np.all(exact - tv == table[None, None].astype(np.float64))
+    ref = np.moveaxis(exact.astype(np.float32), 2, 0)
+    assert np.array_equal(out, ref)
+
+
+# --------------------------------------------------------------------------------------
 # Q/K RMSNorm + interleaved RoPE + joint write
 # --------------------------------------------------------------------------------------
 
