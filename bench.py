@@ -230,16 +230,19 @@ WAN_BYTES = {
     "ln_modulate_per_token": 4 * WAN_ROWS * WAN_D * 2,                       # x, out; scale, shift
     "rmsnorm_tanh_residual_per_token": 4 * WAN_ROWS * WAN_D * 2 + WAN_D * 2,  # x, res, out, gate; w
     "rmsnorm_tanh_residual_per_batch": 3 * WAN_ROWS * WAN_D * 2 + 2 * WAN_D * 2,
+    # bf16 time embedding in, six float32 rows out, the float32 table
+    "wan_modulation_table": 6 * WAN_ROWS * WAN_D * (2 + 4) + 6 * WAN_D * 4,
 }
 
 
 def time_wan(m, torch, mode, reps=10, sample=8):
-    """The Wan 720p kernels at full size: two rotating input sets (~9 GB, far
-    beyond the Infinity Cache) drawn on the device from a seeded generator
-    (N(0, 1) rows, N(0, 0.1) modulation, U(0.5, 1.5) weight, the workload's
-    distributions; host generation of 774 MB tensors would dominate the
-    run), each dispatch timed by its own events; `sample` rows of every
-    output are checked bit for bit against the oracle."""
+    """The Wan 720p kernels at full size: two rotating input sets (~9 GB for
+    the norms, ~28 GB for the modulation table; far beyond the Infinity
+    Cache) drawn on the device from a seeded generator (N(0, 1) rows,
+    N(0, 0.1) modulation, N(0, 0.3) time embedding, U(0.5, 1.5) weight;
+    host generation of 774 MB tensors would dominate the run), each dispatch
+    timed by its own events; `sample` rows (tokens) of every output are
+    checked bit for bit against the oracle."""
     import oracle
     R, Dw = WAN_ROWS, WAN_D
     gen = torch.Generator(device="cuda").manual_seed(4000)
@@ -262,6 +265,11 @@ def time_wan(m, torch, mode, reps=10, sample=8):
         "rmsnorm_tanh_residual_per_batch": lambda s: m.dit_rmsnorm_tanh_residual(
             s["x"], s["res"], s["w"], s["g1"], EPS, mode, out=s["out"], prepare=True),
     }
+    mt = [dict(table=torch.randn((6, Dw), device="cuda", generator=gen) * 0.05,
+               temb=bf((1, R, 6, Dw), 0.3),
+               out=torch.empty((6, 1, R, Dw), dtype=torch.float32, device="cuda"))
+          for _ in range(2)]
+    ops["wan_modulation_table"] = None
     rows = np.linspace(0, R - 1, sample).astype(np.int64)
 
     def host(t):
@@ -269,7 +277,11 @@ def time_wan(m, torch, mode, reps=10, sample=8):
 
     res = {}
     for k, mk in ops.items():
-        plans = [mk(s) for s in sets]
+        if k == "wan_modulation_table":
+            plans = [m.dit_wan_modulation_table(t["table"], t["temb"], out=t["out"], prepare=True)
+                     for t in mt]
+        else:
+            plans = [mk(s) for s in sets]
         for i in range(3):
             plans[i % 2]()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
@@ -285,7 +297,14 @@ def time_wan(m, torch, mode, reps=10, sample=8):
         us = float(np.mean(us_list))
         gbs = WAN_BYTES[k] / (us * 1e-6) / 1e9
         exact = None
-        if mode == "lossless":
+        if k == "wan_modulation_table":
+            t = mt[(reps - 1) % 2]
+            idx = torch.from_numpy(rows).cuda()
+            ref = oracle.wan_mod_table(t["table"].cpu().numpy(),
+                                       host(t["temb"].index_select(1, idx)))
+            got = t["out"].index_select(2, idx).cpu().numpy()
+            exact = bool(np.array_equal(got.view(np.uint32), ref.view(np.uint32)))
+        elif mode == "lossless":
             s = sets[(reps - 1) % 2]
             idx = torch.from_numpy(rows).cuda()
             sel = {n: host(s[n].index_select(0, idx)) for n in ("x", "res", "sc", "sh", "gt",
@@ -303,8 +322,22 @@ def time_wan(m, torch, mode, reps=10, sample=8):
                       bytes=WAN_BYTES[k], gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
                       rows_per_s=float("%.4g" % (R / (us * 1e-6))),
                       bit_exact_sampled_rows=exact)
+        if k == "wan_modulation_table":
+            # the unfused expression it replaces: a float32 temporary, then the
+            # six chunks made contiguous (torch, for context)
+            t = mt[0]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for rep in range(2):
+                torch.cuda.synchronize()
+                e0.record()
+                tmp = t["table"].view(1, 1, 6, Dw) + t["temb"].float()
+                chunks = [c.contiguous() for c in tmp.chunk(6, dim=2)]
+                e1.record()
+                torch.cuda.synchronize()
+                del tmp, chunks
+            res[k]["unfused_torch_us"] = round(1000.0 * e0.elapsed_time(e1), 1)
         del plans
-    del sets
+    del sets, mt
     torch.cuda.empty_cache()
     return res
 

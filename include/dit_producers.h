@@ -70,6 +70,24 @@ dit_status_t dit_gate_add_ln_modulate_fp8(
     const void *gate, const void *scale, const void *shift, int64_t mod_rs, int64_t mod_rows,
     int64_t rows, int64_t dim, float eps, const float *fp8_scale, int mode, hipStream_t stream);
 
+/*
+ * Wan per-token modulation table  [P1 Wan视频模型的数据搬运优化]
+ *   out[k][b][s][i] = table[k][i] + temb[b][s][k][i]     (one binary32 add)
+ * The block's modulation table plus the per-token time embedding, written
+ * as n_mod (6 in Wan) contiguous [batch, tokens, dim] tensors: the layout
+ * the per-token modulated norms read, with no temporary and no chunked,
+ * strided views to make contiguous later.  The addition is the one the
+ * unfused expression performs, so the result is bit-identical to it.
+ * table: [n_mod, dim] float32; temb: [batch, tokens, n_mod, dim] bf16;
+ * out: [n_mod, batch, tokens, dim] float32; all contiguous, 16-byte
+ * aligned, dim % 8 == 0 (else DIT_ERR_UNSUPPORTED); out must not overlap an
+ * input (DIT_ERR_INVALID).  Empty problems return DIT_OK.  Independent of
+ * the numerics mode (a single IEEE addition).
+ */
+dit_status_t dit_wan_modulation_table(float *out, const float *table, const void *temb,
+                                      int64_t batch, int64_t tokens, int64_t n_mod, int64_t dim,
+                                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,7 @@ SIGNATURES = {
     "dit_gate_add_ln_modulate_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                      _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _int, _vp],
     "dit_probe_fp8": [_int, _vp, _vp, _i64, _vp, _vp],
+    "dit_wan_modulation_table": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
                          ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
     "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
@@ -356,6 +357,26 @@ def dit_gate_add_ln_modulate_fp8(residual, y, gate, scale, shift, fp8_scale, eps
                  residual.data_ptr(), r_rs, y.data_ptr(), y_rs, gate.data_ptr(),
                  scale.data_ptr(), shift.data_ptr(), mrs, mrows, rows, dim, eps, fs.data_ptr(),
                  _mode(mode), _stream(residual))
+
+
+def dit_wan_modulation_table(table, temb, out=None, prepare=False):
+    """table: float32 [n_mod, D] (contiguous); temb: bfloat16 [B, S, n_mod, D]
+    (contiguous).  Returns float32 [n_mod, B, S, D] = table[k] + temb[:, :, k]."""
+    if table.dtype != torch.float32 or table.dim() != 2 or not table.is_contiguous():
+        raise DitUnsupported("table must be a contiguous float32 [n_mod, D] tensor")
+    if temb.dtype != torch.bfloat16 or temb.dim() != 4 or not temb.is_contiguous():
+        raise DitUnsupported("temb must be a contiguous bfloat16 [B, S, n_mod, D] tensor")
+    B, S, K, D = temb.shape
+    if tuple(table.shape) != (K, D):
+        raise DitInvalid(f"table shape {tuple(table.shape)} does not match temb {tuple(temb.shape)}")
+    _same_device(table, temb)
+    if out is None:
+        out = torch.empty((K, B, S, D), dtype=torch.float32, device=temb.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (K, B, S, D) or not out.is_contiguous():
+        raise DitInvalid("out must be a contiguous float32 [n_mod, B, S, D] tensor")
+    _same_device(temb, out)
+    return _call("dit_wan_modulation_table", out, prepare, out.data_ptr(), table.data_ptr(),
+                 temb.data_ptr(), B, S, K, D, _stream(temb))
 
 
 def _qkv_stream(st):

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 
 SOURCES = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_qkv.hip",
-           "dit_probe.hip", "dit_abi.cpp"]
+           "dit_modtab.hip", "dit_probe.hip", "dit_abi.cpp"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -305,6 +305,30 @@ dit_status_t check_fp8(void *out8, int64_t out8_rs, const float *fp8_scale, int6
 
 extern "C" {
 
+dit_status_t dit_wan_modulation_table(float *out, const float *table, const void *temb,
+                                      int64_t batch, int64_t tokens, int64_t n_mod, int64_t dim,
+                                      hipStream_t stream) {
+  if (batch < 0 || tokens < 0 || n_mod < 0 || dim < 0)
+    return fail(DIT_ERR_INVALID, "negative size");
+  if (batch == 0 || tokens == 0 || n_mod == 0) return DIT_OK;
+  if (dim == 0 || dim % 8 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "dim must be a positive multiple of 8");
+  if (!out || !table || !temb) return fail(DIT_ERR_INVALID, "NULL pointer");
+  if (!aligned16(out) || !aligned16(table) || !aligned16(temb))
+    return fail(DIT_ERR_UNSUPPORTED, "tensor pointer is not 16-byte aligned");
+  if (n_mod > 64) return fail(DIT_ERR_UNSUPPORTED, "n_mod > 64");
+  if (batch > (int64_t(1) << 32) / tokens || dim > 65536)
+    return fail(DIT_ERR_UNSUPPORTED, "problem too large");
+  const int64_t n = n_mod * batch * tokens * dim;
+  const Span so{reinterpret_cast<uintptr_t>(out), 0, 1, n * 4};
+  const Span st{reinterpret_cast<uintptr_t>(table), 0, 1, n_mod * dim * 4};
+  const Span se{reinterpret_cast<uintptr_t>(temb), 0, 1, n * 2};
+  if (spans_overlap(so, st) || spans_overlap(so, se))
+    return fail(DIT_ERR_INVALID, "out overlaps an input");
+  dit::ModTableArgs a{out, table, u16(temb), batch, tokens, n_mod, dim};
+  return hip_status(dit::launch_wan_mod_table(a, stream));
+}
+
 dit_status_t dit_ln_modulate_fp8(void *out, int64_t out_rs, void *out_fp8, int64_t out_fp8_rs,
                                  const void *x, int64_t x_rs, const void *scale,
                                  const void *shift, int64_t mod_rs, int64_t mod_rows,

@@ -99,6 +99,14 @@ struct QkvArgs {
   int64_t parts;               // set by the launcher: waves sharing one token's heads
 };
 
+struct ModTableArgs {
+  float *out;                  // [n_mod, batch, tokens, dim]
+  const float *table;          // [n_mod, dim]
+  const uint16_t *temb;        // [batch, tokens, n_mod, dim] bf16
+  int64_t batch, tokens, n_mod, dim;
+};
+
+hipError_t launch_wan_mod_table(const ModTableArgs &a, hipStream_t s);
 hipError_t launch_ln_modulate(const LnModArgs &a, int mode, hipStream_t s);
 hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_t s);
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s);

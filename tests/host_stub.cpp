@@ -62,6 +62,12 @@ hipError_t launch_qk_norm_rope(const QkvArgs &a, int mode, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_wan_mod_table(const ModTableArgs &a, hipStream_t) {
+  const int64_t v[] = {a.batch, a.tokens, a.n_mod, a.dim};
+  rec("wan_mod_table", 0, v, 4);
+  return hipSuccess;
+}
+
 hipError_t launch_probe_fp8(int op, uint8_t *, const void *, int64_t n, const float *,
                             hipStream_t) {
   rec("probe_fp8", op, &n, 1);

@@ -69,6 +69,7 @@ def stub(tmp_path_factory):
     lib.dit_gate_add_ln_modulate_fp8.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                                  vp, vp, i64, i64, i64, i64, f32, vp, cint, vp]
     lib.dit_probe_fp8.argtypes = [cint, vp, vp, i64, vp, vp]
+    lib.dit_wan_modulation_table.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
     return lib
 
 
@@ -253,6 +254,26 @@ def test_probe_fp8_guards(stub):
     assert stub.dit_probe_fp8(1, Q8, X, 16, None, None) == INVALID    # quant needs the scale
     assert stub.dit_probe_fp8(0, Q8, X, 16, None, None) == OK
     assert stub.dit_probe_fp8(0, Q8, X, 0, None, None) == OK
+
+
+def test_wan_modulation_table_guards(stub):
+    r = Rec(stub)
+    f = stub.dit_wan_modulation_table
+    n0 = r.calls
+    assert f(OUT, W, X, 1, 100, 6, 512, None) == OK
+    assert r.calls == n0 + 1 and r.name == "wan_mod_table" and r.vals[:4] == [1, 100, 6, 512]
+    for args, status, why in [
+            ((OUT, W, X, 1, 100, 6, 516, None), UNSUPPORTED, "multiple of 8"),
+            ((OUT, W, X, -1, 100, 6, 512, None), INVALID, "negative"),
+            ((0, W, X, 1, 100, 6, 512, None), INVALID, "NULL"),
+            ((OUT + 8, W, X, 1, 100, 6, 512, None), UNSUPPORTED, "aligned"),
+            ((X, W, X, 1, 100, 6, 512, None), INVALID, "overlaps"),
+            ((W - 4096, W, X, 1, 100, 6, 512, None), INVALID, "overlaps")]:
+        n0 = r.calls
+        assert f(*args) == status, args
+        assert r.calls == n0
+        assert why.lower() in stub.dit_status_reason().decode().lower(), (args, why)
+    assert f(OUT, W, X, 0, 100, 6, 512, None) == OK                   # empty
 
 
 class Stream(ctypes.Structure):

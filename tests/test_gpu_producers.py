@@ -253,3 +253,43 @@ def test_fp8_qwen_block_full_size():
     assert_bits_equal(host(rp), refs[0], "qwen r'")
     assert_bits_equal(host(out), refs[1], "qwen out")
     _e4m3_equal(_u8(q), refs[2], "qwen e4m3")
+
+
+# --------------------------------------------------------------------------------------
+# Wan per-token modulation table (page "基于Agent的SGLang扩散模型Kernel优化实践", section
+# "Wan视频模型的数据搬运优化")
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,K,D", [(1, 1, 6, 8), (1, 37, 6, 520), (2, 100, 6, 3072),
+                                     (1, 300, 6, 5120), (3, 7, 2, 1032)])
+def test_wan_modulation_table_shapes(B, S, K, D):
+    say("wan modulation table", B, S, K, D)
+    rng = np.random.default_rng(B * 1000 + S + D)
+    table = (rng.standard_normal((K, D)) * 0.05).astype(np.float32)
+    temb = synth.normal_bf16((B, S, K, D), 0.3, 7000 + S)
+    got = m().dit_wan_modulation_table(torch.from_numpy(table).cuda(), dev(temb))
+    ref = oracle.wan_mod_table(table, temb)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_wan_modulation_table_full_size():
+    """The Wan 720p block: 75600 tokens x 6 x 5120 (4.6 GB in, 9.3 GB out),
+    inputs drawn on the device; every element against torch's binary32
+    addition of the same operands (the unfused expression), and sampled
+    tokens against the oracle."""
+    say("wan modulation table [1, 75600, 6, 5120]")
+    g = torch.Generator(device="cuda").manual_seed(4100)
+    table = torch.randn((6, 5120), device="cuda", generator=g) * 0.05
+    temb = (torch.randn((1, 75600, 6, 5120), device="cuda", generator=g) * 0.3).to(
+        torch.bfloat16)
+    out = m().dit_wan_modulation_table(table, temb)
+    for k in range(6):
+        ref = table[k][None, None, :] + temb[:, :, k, :].float()
+        assert torch.equal(out[k].view(torch.int32), ref.view(torch.int32)), k
+        del ref
+    tok = torch.tensor([0, 1, 37777, 75599], device="cuda")
+    t_h = table.cpu().numpy()
+    e_h = host(temb.index_select(1, tok))
+    ref = oracle.wan_mod_table(t_h, e_h)
+    got = out.index_select(2, tok).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
