@@ -80,10 +80,17 @@ def load(path=None):
                                              ctypes.c_float]
     lib.orc_wan_mod_table.restype = ctypes.c_int
     lib.orc_wan_mod_table.argtypes = [_f32p, _f32p, _u16p, _i64, _i64, _i64, _i64]
+    lib.orc_modulate_scale_shift.restype = ctypes.c_int
+    lib.orc_modulate_scale_shift.argtypes = [_u16p, _i64, _u16p, _i64, _u16p, _u16p, _i64, _i64,
+                                             _i64, _i64]
     lib.orc_qk_norm_rope.restype = ctypes.c_int
     lib.orc_qk_norm_rope.argtypes = [_u16p, _u16p, _u16p, _i64, _i64,
                                      ctypes.POINTER(QkvStream), ctypes.POINTER(QkvStream),
                                      _f32p, _f32p, _i64, _i64, _i64, ctypes.c_float]
+    lib.orc_qk_norm_rope_dest.restype = ctypes.c_int
+    lib.orc_qk_norm_rope_dest.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
+                                          ctypes.POINTER(QkvStream), ctypes.POINTER(QkvStream),
+                                          _f32p, _f32p, _i64, _i64, _i64, ctypes.c_float]
     lib.orc_bf16_round_array.argtypes = [_f32p, _u16p, _i64]
     lib.orc_bf16_round_bits_range.argtypes = [ctypes.c_uint32, _i64, _u16p]
     lib.orc_e4m3.restype = ctypes.c_uint8
@@ -285,6 +292,19 @@ def ln_modulate(x, scale, shift, eps=1e-6):
     return out
 
 
+def modulate_scale_shift(x, scale, shift):
+    """x [rows, D]; scale, shift [mod_rows, D] -> bf(bf(x * bf(1 + scale)) + shift)."""
+    x_rs, x = _rows(x)
+    rows, dim = x.shape
+    m_rs, scale = _mod(scale, dim)
+    m_rs2, shift = _mod(shift, dim)
+    assert m_rs == m_rs2 and scale.shape == shift.shape
+    out = np.empty((rows, dim), dtype=np.uint16)
+    _check(load().orc_modulate_scale_shift(_p16(out), dim, _p16(x), x_rs, _p16(scale),
+                                           _p16(shift), m_rs, scale.shape[0], rows, dim))
+    return out
+
+
 def rmsnorm_scale(x, w, scale, eps=1e-6):
     x_rs, x = _rows(x)
     rows, dim = x.shape
@@ -419,3 +439,31 @@ def qk_norm_rope(txt, img, cos_t, sin_t, eps=1e-6):
                                    _p32(sin_t), B, H, Dh, ctypes.c_float(eps)))
     del tk, ik
     return tuple(outs)
+
+
+def qk_norm_rope_packed(txt, img, cos_t, sin_t, dests, eps=1e-6):
+    """The QKV epilogue written destination-major: returns the packed buffer
+    [P, B, S_txt + S_img, 3, H / P, Dh] (P = dests) whose chunk p holds
+    heads p H/P .. (p + 1) H/P - 1 of q, k, v."""
+    B, S_txt, H, Dh = txt["q"].shape
+    S_img = img["q"].shape[1]
+    S = S_txt + S_img
+    assert H % dests == 0
+    hpd = H // dests
+    buf = np.empty((dests, B, S, 3, hpd, Dh), dtype=np.uint16)
+    ts, tk = _stream(txt["q"], txt["k"], txt["v"], np.ascontiguousarray(txt["q_weight"]),
+                     np.ascontiguousarray(txt["k_weight"]))
+    ist, ik = _stream(img["q"], img["k"], img["v"], np.ascontiguousarray(img["q_weight"]),
+                      np.ascontiguousarray(img["k_weight"]))
+    cos_t = np.ascontiguousarray(cos_t, dtype=np.float32)
+    sin_t = np.ascontiguousarray(sin_t, dtype=np.float32)
+    base = buf.reshape(-1)
+    q = base[0:].ctypes.data_as(_u16p)
+    k = base[hpd * Dh:].ctypes.data_as(_u16p)
+    v = base[2 * hpd * Dh:].ctypes.data_as(_u16p)
+    _check(load().orc_qk_norm_rope_dest(q, k, v, 3 * hpd * Dh, S * 3 * hpd * Dh, hpd,
+                                        B * S * 3 * hpd * Dh, ctypes.byref(ts),
+                                        ctypes.byref(ist), _p32(cos_t), _p32(sin_t), B, H, Dh,
+                                        ctypes.c_float(eps)))
+    del tk, ik
+    return buf

@@ -328,6 +328,32 @@ int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *ou
 }
 
 /* ------------------------------------------------------------------------- */
+/* Standalone AdaLN modulate  [P3 实现拆解: modulate_scale_shift, the shared     */
+/*  fast path behind the models' x * (1 + scale) + shift; with the rounding    */
+/*  points of the eager bf16 chain, P1 数学等价不代表结果完全一致]                */
+/* ------------------------------------------------------------------------- */
+
+/* out = bf(bf(x * bf(1 + scale)) + shift), row r using modulation row
+ * r / (rows / mod_rows). */
+int orc_modulate_scale_shift(uint16_t *out, int64_t out_rs, const uint16_t *x, int64_t x_rs,
+                             const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
+                             int64_t mod_rows, int64_t rows, int64_t dim) {
+  if (rows <= 0 || dim <= 0 || mod_rows <= 0 || rows % mod_rows) return 1;
+  int64_t per_mod = rows / mod_rows;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t m = r / per_mod;               /* modulation row */
+    const uint16_t *sc = scale + m * mod_rs, *sh = shift + m * mod_rs;
+    for (int64_t i = 0; i < dim; ++i) {
+      const float one_plus = orc_bf16_value(orc_one_plus(sc[i]));
+      float p = bfv(orc_bf16_value(x[r * x_rs + i]) * one_plus);
+      const float sum = p + orc_bf16_value(sh[i]);
+      out[r * out_rs + i] = orc_bf16_round(sum);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* BF16 + static E4M3 dual-output producers                                  */
 /* [P1 将FP8量化融合到前序算子: LayerNorm/AdaLN and gated residual +            */
 /*  LayerNorm/AdaLN also write a statically scaled E4M3 copy of their BF16     */
@@ -462,7 +488,7 @@ void orc_qk_head(const uint16_t *x, const uint16_t *w, const float *c, const flo
 static void qkv_stream(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_t out_ts,
                        int64_t out_bs, const orc_qkv_stream *st, int64_t joint_first,
                        const float *cos_t, const float *sin_t, int64_t batch, int64_t heads,
-                       int64_t Dh, float eps) {
+                       int64_t Dh, float eps, int64_t hpd, int64_t dest_stride) {
   int64_t half = Dh / 2;
   for (int64_t b = 0; b < batch; ++b)
     for (int64_t s = 0; s < st->tokens; ++s) {
@@ -472,27 +498,49 @@ static void qkv_stream(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_
       int64_t src = b * st->batch_stride + s * st->tok_stride;
       int64_t dst = b * out_bs + jt * out_ts;
       for (int64_t h = 0; h < heads; ++h) {
-        orc_qk_head(st->q + src + h * Dh, st->q_weight, c, z, Dh, eps, q_out + dst + h * Dh);
-        orc_qk_head(st->k + src + h * Dh, st->k_weight, c, z, Dh, eps, k_out + dst + h * Dh);
-        memcpy(v_out + dst + h * Dh, st->v + src + h * Dh, sizeof(uint16_t) * (size_t)Dh);
+        /* head h of destination h / hpd, position h % hpd within it */
+        int64_t ho = dst + (h / hpd) * dest_stride + (h % hpd) * Dh;
+        orc_qk_head(st->q + src + h * Dh, st->q_weight, c, z, Dh, eps, q_out + ho);
+        orc_qk_head(st->k + src + h * Dh, st->k_weight, c, z, Dh, eps, k_out + ho);
+        memcpy(v_out + ho, st->v + src + h * Dh, sizeof(uint16_t) * (size_t)Dh);
       }
     }
 }
 
-/* Text tokens occupy joint rows [0, S_txt), image tokens [S_txt, S_txt+S_img). */
+/* Text tokens occupy joint rows [0, S_txt), image tokens [S_txt, S_txt+S_img):
+ * the destination-major form below with a single destination. */
 int orc_qk_norm_rope(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_t out_tok_stride,
                      int64_t out_batch_stride, const orc_qkv_stream *txt,
                      const orc_qkv_stream *img, const float *cos_t, const float *sin_t,
                      int64_t batch, int64_t heads, int64_t head_dim, float eps) {
+  return orc_qk_norm_rope_dest(q_out, k_out, v_out, out_tok_stride, out_batch_stride,
+                               heads > 0 ? heads : 1, 0, txt, img, cos_t, sin_t, batch, heads,
+                               head_dim, eps);
+}
+
+/* The same epilogue written destination-major for Ulysses sequence
+ * parallelism [P1 Ulysses QKV仅执行一次All-to-All]: the heads are split into
+ * heads / hpd destinations of hpd heads each; head h goes to destination
+ * h / hpd, which starts dest_stride elements after the previous one, at
+ * head position h % hpd.  With q_out, k_out, v_out interleaved per token
+ * this is the packed [P][B, S, 3, hpd, Dh] buffer whose chunk p an
+ * all-to-all sends to rank p. */
+int orc_qk_norm_rope_dest(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out,
+                          int64_t out_tok_stride, int64_t out_batch_stride, int64_t hpd,
+                          int64_t dest_stride, const orc_qkv_stream *txt,
+                          const orc_qkv_stream *img, const float *cos_t, const float *sin_t,
+                          int64_t batch, int64_t heads, int64_t head_dim, float eps) {
   if (head_dim < 8 || head_dim > 512 || head_dim % 8) return 1;
   int64_t lanes = head_dim / 8;
   if (lanes & (lanes - 1)) return 1;
+  if (hpd <= 0 || heads % hpd) return 1;
   if (txt && txt->tokens > 0)
     qkv_stream(q_out, k_out, v_out, out_tok_stride, out_batch_stride, txt, 0, cos_t, sin_t,
-               batch, heads, head_dim, eps);
+               batch, heads, head_dim, eps, hpd, dest_stride);
   if (img && img->tokens > 0)
     qkv_stream(q_out, k_out, v_out, out_tok_stride, out_batch_stride, img,
-               txt ? txt->tokens : 0, cos_t, sin_t, batch, heads, head_dim, eps);
+               txt ? txt->tokens : 0, cos_t, sin_t, batch, heads, head_dim, eps, hpd,
+               dest_stride);
   return 0;
 }
 

@@ -50,6 +50,9 @@ int orc_gate_add_ln_modulate(uint16_t *out_res, int64_t out_res_rs, uint16_t *ou
                              const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
                              int64_t mod_rows, int64_t rows, int64_t dim, float eps);
 
+int orc_modulate_scale_shift(uint16_t *out, int64_t out_rs, const uint16_t *x, int64_t x_rs,
+                             const uint16_t *scale, const uint16_t *shift, int64_t mod_rs,
+                             int64_t mod_rows, int64_t rows, int64_t dim);
 double orc_e4m3_value(uint8_t c);
 uint8_t orc_e4m3(float v);
 int orc_ln_modulate_fp8(uint16_t *out, int64_t out_rs, uint8_t *out8, int64_t out8_rs,
@@ -78,6 +81,11 @@ int orc_qk_norm_rope(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out, int64_t 
                      int64_t out_batch_stride, const orc_qkv_stream *txt,
                      const orc_qkv_stream *img, const float *cos_t, const float *sin_t,
                      int64_t batch, int64_t heads, int64_t head_dim, float eps);
+int orc_qk_norm_rope_dest(uint16_t *q_out, uint16_t *k_out, uint16_t *v_out,
+                          int64_t out_tok_stride, int64_t out_batch_stride, int64_t hpd,
+                          int64_t dest_stride, const orc_qkv_stream *txt,
+                          const orc_qkv_stream *img, const float *cos_t, const float *sin_t,
+                          int64_t batch, int64_t heads, int64_t head_dim, float eps);
 
 void orc_bf16_round_array(const float *in, uint16_t *out, int64_t n);
 void orc_bf16_round_bits_range(uint32_t first, int64_t n, uint16_t *out);

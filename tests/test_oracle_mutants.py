@@ -95,6 +95,14 @@ MUTANTS = {
         "const float e = orc_bf16_value(temb[((b * tokens + s) * n_mod + k) * dim + i]);",
         "const float e = orc_bf16_value(temb[((b * tokens + s) * n_mod) * dim + i]);",
         ["test_wan_mod_table_layout_with_tagged_values"]),
+    "modulate product not rounded": (
+        "float p = bfv(orc_bf16_value(x[r * x_rs + i]) * one_plus);",
+        "float p = orc_bf16_value(x[r * x_rs + i]) * one_plus;",
+        ["test_modulate_scale_shift_exact_steps"]),
+    "heads dealt to destinations round-robin": (
+        "int64_t ho = dst + (h / hpd) * dest_stride + (h % hpd) * Dh;",
+        "int64_t ho = dst + (h % (heads / hpd)) * dest_stride + (h / (heads / hpd)) * Dh;",
+        ["test_qk_norm_rope_destination_major_layout"]),
     "RoPE sign": (
         "o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);",
         "o[2 * i] = orc_bf16_round(a * c[i] + b * z[i]);",

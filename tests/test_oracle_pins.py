@@ -590,6 +590,41 @@ def test_gate_add_ln_per_batch_equals_repeated_per_token():
 
 
 # --------------------------------------------------------------------------------------
+# Standalone modulate (page "#34085 [diffusion] Clean up kernels and shared fast paths",
+# section "实现拆解": modulate_scale_shift)
+# --------------------------------------------------------------------------------------
+
+def test_modulate_scale_shift_exact_steps():
+    """Each of the three roundings is a single correct rounding of an exact
+    float64 value: 1 + scale, the product of two bf16 values, the sum of two
+    bf16 values.  Per-batch rows (rows 0-5 use modulation row 0)."""
+    rng = np.random.default_rng(150)
+    rows, D = 12, 520
+    x = _rand_bf16(rng, rows * D, 6).reshape(rows, D)
+    scale = nearest_bf16(rng.standard_normal((2, D)) * 0.3).reshape(2, D)
+    shift = _rand_bf16(rng, 2 * D, 4).reshape(2, D)
+    out = oracle.modulate_scale_shift(x, scale, shift)
+    sc, sh = np.repeat(scale, 6, axis=0), np.repeat(shift, 6, axis=0)
+    s1 = value_of_bf16(nearest_bf16(1.0 + value_of_bf16(sc)))
+    p = value_of_bf16(nearest_bf16(value_of_bf16(x) * s1))
+    ref = nearest_bf16(p + value_of_bf16(sh)).reshape(rows, D)
+    assert np.array_equal(out, ref)
+
+
+def test_modulate_scale_shift_identities():
+    """scale = 0, shift = -0: x * 1 + (-0) = x bitwise; scale = -1: x * 0 is
+    a zero, so out = shift (shift non-zero, x finite)."""
+    x = synth.normal_bf16((8, 1032), 1.0, 151)
+    zero = np.zeros((1, 1032), dtype=np.uint16)
+    negz = np.full((1, 1032), 0x8000, dtype=np.uint16)
+    assert np.array_equal(oracle.modulate_scale_shift(x, zero, negz), x)
+    shift = _nonzero_shift((1, 1032), 152)
+    minus1 = np.full((1, 1032), 0xBF80, dtype=np.uint16)
+    assert np.array_equal(oracle.modulate_scale_shift(x, minus1, shift),
+                          np.repeat(shift, 8, axis=0))
+
+
+# --------------------------------------------------------------------------------------
 # BF16 + static E4M3 dual output (page "基于Agent的SGLang扩散模型Kernel优化实践", section
 # "将FP8量化融合到前序算子")
 # --------------------------------------------------------------------------------------
@@ -825,3 +860,43 @@ def test_qk_norm_rope_joint_placement_and_v_copy():
                 assert np.array_equal(v[b, j, h], vs)
                 assert np.array_equal(q[b, j, h], oracle.qk_head(qs, wq, cos_t[j], sin_t[j], 1e-6))
                 assert np.array_equal(k[b, j, h], oracle.qk_head(ks, wk, cos_t[j], sin_t[j], 1e-6))
+
+
+def test_qk_norm_rope_destination_major_layout():
+    """Destination-major output for Ulysses sequence parallelism (page
+    "基于Agent的SGLang扩散模型Kernel优化实践", section "Ulysses QKV仅执行一次All-to-All"):
+    chunk p of the packed [P, B, S, 3, H/P, Dh] buffer holds heads p H/P ..
+    (p + 1) H/P - 1 of q, k and v for every token, in the joint order.  Checked
+    against the plain joint outputs through an independent index permutation,
+    and V (a bit copy) against its source heads directly."""
+    rng = np.random.default_rng(121)
+    B, S_txt, S_img, H, Dh = 2, 3, 5, 8, 128
+    W = 3 * H * Dh
+    txt = nearest_bf16(rng.standard_normal(B * S_txt * W)).reshape(B, S_txt, W)
+    img = nearest_bf16(rng.standard_normal(B * S_img * W)).reshape(B, S_img, W)
+    wts = [nearest_bf16(rng.uniform(0.5, 1.5, Dh)) for _ in range(4)]
+    ang = rng.uniform(-3, 3, (S_txt + S_img, Dh // 2))
+    cos_t, sin_t = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+    def views(a):
+        b, s, _ = a.shape
+        return [a[:, :, i * H * Dh:(i + 1) * H * Dh].reshape(b, s, H, Dh) for i in range(3)]
+
+    tq, tk, tv = views(txt)
+    iq, ik, iv = views(img)
+    ts = dict(q=tq, k=tk, v=tv, q_weight=wts[0], k_weight=wts[1])
+    ims = dict(q=iq, k=ik, v=iv, q_weight=wts[2], k_weight=wts[3])
+    joint = np.stack(oracle.qk_norm_rope(ts, ims, cos_t, sin_t), axis=2)   # [B, S, 3, H, Dh]
+    for P in (1, 2, 4, 8):
+        packed = oracle.qk_norm_rope_packed(ts, ims, cos_t, sin_t, P)
+        hp = H // P
+        assert packed.shape == (P, B, S_txt + S_img, 3, hp, Dh)
+        ref = np.moveaxis(joint.reshape(B, S_txt + S_img, 3, P, hp, Dh), 3, 0)
+        assert np.array_equal(packed, ref), P
+        for p in range(P):
+            for h in range(hp):
+                g = p * hp + h
+                assert np.array_equal(packed[p, :, :S_txt, 2, h],
+                                      txt[:, :, 2 * H * Dh + g * Dh:2 * H * Dh + (g + 1) * Dh])
+                assert np.array_equal(packed[p, :, S_txt:, 2, h],
+                                      img[:, :, 2 * H * Dh + g * Dh:2 * H * Dh + (g + 1) * Dh])
