@@ -24,9 +24,11 @@ names; per-kernel durations (mean, median, p10, p90) come from further steps
 launched eagerly from prepared calls, each dispatch recording its own
 start/stop events, in blocks that interleave the two modes (main, other,
 other, main); the other mode's figures are reported beside them.
-Beside the step, the fused gated residual + LN producer and the Wan 720p
-block's kernels (75600 x 5120, per-token modulation) are timed on their own,
-the latter with 8 sampled rows of each output checked against the oracle.
+Beside the step, the fused producers (gated residual + LN, the E4M3 dual
+outputs), the standalone modulate, the destination-major QKV epilogue and the
+Wan 720p block's kernels (75600 x 5120, per-token modulation, the modulation
+table) are timed on their own, the latter with 8 sampled rows of each output
+checked against the oracle.
 The CPU baseline runs the oracle (plain C) over one full step on the host,
 single-threaded (the reported value) and on all threads of the process's
 CPU share (row blocks in parallel), and compares the GPU's outputs with it
@@ -74,7 +76,12 @@ PRODUCER_BYTES = {
     "ln_modulate_fp8": 2 * ROWS * D * 2 + ROWS * D + 2 * B * D * 2 + 4,
     # residual, y, r', out, E4M3 out; gate, scale, shift; the fp8 scale
     "gate_add_ln_modulate_fp8": 4 * ROWS * D * 2 + ROWS * D + 3 * B * D * 2 + 4,
+    # standalone modulate: x, out; scale, shift
+    "modulate_scale_shift": 2 * ROWS * D * 2 + 2 * B * D * 2,
+    # the QKV epilogue written destination-major for ULYSSES_P ranks: same bytes
+    "qk_norm_rope_packed": BYTES["qk_norm_rope"],
 }
+ULYSSES_P = 4         # Ulysses degree of the destination-major QKV line (6 heads per rank)
 FP8_SCALE = 0.0173    # static per-tensor scale of the E4M3 outputs
 
 
@@ -190,6 +197,8 @@ def time_producers(m, torch, sets, mode, steps):
 
     fs = torch.tensor([FP8_SCALE], dtype=torch.float32, device="cuda")
     q8 = [torch.empty((ROWS, D), dtype=torch.float8_e4m3fn, device="cuda") for _ in sets]
+    packed = [torch.empty((ULYSSES_P, B, S_TXT + S_IMG, 3, H // ULYSSES_P, DH),
+                          dtype=torch.bfloat16, device="cuda") for _ in sets]
     plans = {
         "gate_add_ln_modulate": [m.dit_gate_add_ln_modulate(
             s.res, s.y, s.gate, s.scale, s.shift, EPS, mode, out_residual=s.prod["residual"],
@@ -201,6 +210,11 @@ def time_producers(m, torch, sets, mode, steps):
             s.res, s.y, s.gate, s.scale, s.shift, fs, EPS, mode,
             out_residual=s.prod["residual"], out=s.prod["out"], out_fp8=q, prepare=True)
             for s, q in zip(sets, q8)],
+        "modulate_scale_shift": [m.dit_modulate_scale_shift(
+            s.x, s.scale, s.shift, mode, out=s.prod["out"], prepare=True) for s in sets],
+        "qk_norm_rope_packed": [m.dit_qk_norm_rope_packed(
+            s.txt, s.img, s.cos, s.sin, ULYSSES_P, EPS, mode, out=pk, prepare=True)
+            for s, pk in zip(sets, packed)],
     }
     gate = [m.dit_residual_gate_add(s.res, s.y, s.gate, mode, out=s.prod["residual"],
                                     prepare=True) for s in sets]
@@ -219,8 +233,9 @@ def time_producers(m, torch, sets, mode, steps):
     pair_us, _ = run([gate, ln])
     res["gate_add_ln_modulate"]["unfused_pair_us"] = round(pair_us, 2)
     res["note"] = ("back to back; gate_add_ln_modulate replaces residual_gate_add + "
-                   "ln_modulate (unfused_pair_us); fp8 variants add an E4M3 copy, scale %g"
-                   % FP8_SCALE)
+                   "ln_modulate (unfused_pair_us); fp8 variants add an E4M3 copy, scale %g; "
+                   "qk_norm_rope_packed writes the destination-major [P, B, S, 3, H/P, 128] "
+                   "buffer for P = %d" % (FP8_SCALE, ULYSSES_P))
     return res
 
 
@@ -228,6 +243,7 @@ def time_producers(m, torch, sets, mode, steps):
 WAN_ROWS, WAN_D = 75600, 5120
 WAN_BYTES = {
     "ln_modulate_per_token": 4 * WAN_ROWS * WAN_D * 2,                       # x, out; scale, shift
+    "modulate_scale_shift_per_token": 4 * WAN_ROWS * WAN_D * 2,              # x, out; scale, shift
     "rmsnorm_tanh_residual_per_token": 4 * WAN_ROWS * WAN_D * 2 + WAN_D * 2,  # x, res, out, gate; w
     "rmsnorm_tanh_residual_per_batch": 3 * WAN_ROWS * WAN_D * 2 + 2 * WAN_D * 2,
     # bf16 time embedding in, six float32 rows out, the float32 table
@@ -260,6 +276,8 @@ def time_wan(m, torch, mode, reps=10, sample=8):
     ops = {
         "ln_modulate_per_token": lambda s: m.dit_ln_modulate(
             s["x"], s["sc"], s["sh"], EPS, mode, out=s["out"], prepare=True),
+        "modulate_scale_shift_per_token": lambda s: m.dit_modulate_scale_shift(
+            s["x"], s["sc"], s["sh"], mode, out=s["out"], prepare=True),
         "rmsnorm_tanh_residual_per_token": lambda s: m.dit_rmsnorm_tanh_residual(
             s["x"], s["res"], s["w"], s["gt"], EPS, mode, out=s["out"], prepare=True),
         "rmsnorm_tanh_residual_per_batch": lambda s: m.dit_rmsnorm_tanh_residual(
@@ -311,6 +329,8 @@ def time_wan(m, torch, mode, reps=10, sample=8):
                                                                "out")}
             if k == "ln_modulate_per_token":
                 ref = oracle.ln_modulate(sel["x"], sel["sc"], sel["sh"], EPS)
+            elif k == "modulate_scale_shift_per_token":
+                ref = oracle.modulate_scale_shift(sel["x"], sel["sc"], sel["sh"])
             elif k == "rmsnorm_tanh_residual_per_token":
                 ref = oracle.rmsnorm_tanh_residual(sel["x"], sel["res"], host(s["w"]), sel["gt"],
                                                    EPS)

@@ -12,6 +12,10 @@
  *   dit_qk_norm_rope           Q/K RMSNorm per head, interleaved RoPE, V copy,
  *                              text and image tokens written to joint Q/K/V
  *
+ * and two companions: dit_modulate_scale_shift (the AdaLN modulate alone,
+ * after a norm computed elsewhere) and dit_qk_norm_rope_dest (the QKV
+ * epilogue writing a destination-major buffer for Ulysses all-to-all).
+ *
  * Sources (web pages on SGLang's diffusion kernels):
  *   [P1] "基于Agent的SGLang扩散模型Kernel优化实践：Qwen-Image、FLUX.2和视频模型"
  *        (tahou.com): section "数学等价不代表结果完全一致" (AdaLN and the bf16
@@ -87,7 +91,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 2
+#define DIT_ABI_VERSION 3
 #define DIT_MAX_DIM 8192
 #define DIT_QK_HEAD_DIM 128
 
@@ -169,6 +173,19 @@ dit_status_t dit_residual_gate_add(void *out, int64_t out_rs, const void *residu
                                    int mode, hipStream_t stream);
 
 /*
+ * Standalone AdaLN modulate  [P3 实现拆解 modulate_scale_shift; P1 数学等价不代表结果完全一致]
+ *   out = bf( bf(x * bf(1 + scale[m])) + shift[m] )
+ * x, out: [rows, dim] flat rows; scale, shift: [mod_rows, dim], row stride
+ * mod_rs; row r uses modulation row m = r / (rows / mod_rows).  The three
+ * roundings are those of the eager bf16 chain x * (1 + scale) + shift;
+ * both modes compute them identically.  out may be exactly x (in place).
+ */
+dit_status_t dit_modulate_scale_shift(void *out, int64_t out_rs, const void *x, int64_t x_rs,
+                                      const void *scale, const void *shift, int64_t mod_rs,
+                                      int64_t mod_rows, int64_t rows, int64_t dim, int mode,
+                                      hipStream_t stream);
+
+/*
  * One token stream (text or image) of the merged QKV projection output.
  * q, k, v: [batch, tokens, heads, head_dim] views (head stride head_dim,
  * element stride 1) sharing tok_stride and batch_stride (elements); for a
@@ -202,7 +219,10 @@ typedef struct {
  *   shared by the three; they may interleave inside one buffer).
  * cos, sin: float32 [txt->tokens + img->tokens, 64], contiguous, indexed by
  *   joint token.  Either stream may have zero tokens (or be NULL).
- * Outputs must not overlap any input or each other (DIT_ERR_INVALID).
+ * Outputs must not overlap any input or each other (DIT_ERR_INVALID).  The
+ *   output strides must nest (the larger one at least spans every row of the
+ *   smaller, the smaller at least a token's heads*128 elements), so no output
+ *   overlaps itself (DIT_ERR_UNSUPPORTED).
  * FAST mode: fused multiply-add in the head sum and the rotation, rsqrt.
  */
 dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out, int64_t out_tok_stride,
@@ -210,6 +230,33 @@ dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out, int64_t out
                               const dit_qkv_stream_t *img, const float *cos, const float *sin,
                               int64_t batch, int64_t heads, int64_t head_dim, float eps, int mode,
                               hipStream_t stream);
+
+/*
+ * The same epilogue written destination-major  [P1 Ulysses QKV仅执行一次All-to-All]
+ * The heads are dealt in contiguous groups of heads_per_dest to P = heads /
+ * heads_per_dest destinations (ranks of a Ulysses group): head h goes to
+ * destination p = h / heads_per_dest, at head position h % heads_per_dest,
+ * i.e. element offset
+ *   p * dest_stride + b * out_batch_stride + t * out_tok_stride
+ *     + (h % heads_per_dest) * 128
+ * from q_out (k_out, v_out).  Values are exactly those of dit_qk_norm_rope.
+ * The packed buffer [P][B, S, 3, H/P, 128] that one all-to-all can send,
+ * chunk p to rank p, is q_out = buf, k_out = buf + (H/P)*128, v_out = buf +
+ * 2*(H/P)*128, out_tok_stride = 3*(H/P)*128, out_batch_stride = S *
+ * out_tok_stride, dest_stride = B * out_batch_stride.
+ * heads_per_dest must divide heads (DIT_ERR_INVALID); dest_stride >= 0, a
+ * multiple of 8 when P > 1 (ignored when P = 1).  The three strides must
+ * nest as above with (heads_per_dest * 128) as a token's width, so that no
+ * output overlaps itself (DIT_ERR_UNSUPPORTED).  Other rules as for
+ * dit_qk_norm_rope; heads_per_dest = heads with dest_stride 0 is exactly
+ * dit_qk_norm_rope.
+ */
+dit_status_t dit_qk_norm_rope_dest(void *q_out, void *k_out, void *v_out, int64_t out_tok_stride,
+                                   int64_t out_batch_stride, int64_t heads_per_dest,
+                                   int64_t dest_stride, const dit_qkv_stream_t *txt,
+                                   const dit_qkv_stream_t *img, const float *cos,
+                                   const float *sin, int64_t batch, int64_t heads,
+                                   int64_t head_dim, float eps, int mode, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,11 @@ SIGNATURES = {
     "dit_wan_modulation_table": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
                          ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
+    "dit_modulate_scale_shift": [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                 _vp],
+    "dit_qk_norm_rope_dest": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.POINTER(QkvStream),
+                              ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int,
+                              _vp],
     "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
     "dit_probe_unary": [_int, _vp, _vp, _i64, _int, _vp],
     "dit_probe_f32": [_int, _vp, _vp, _vp, _i64, _int, _vp],
@@ -266,6 +271,20 @@ def dit_residual_gate_add(residual, y, gate, mode="lossless", out=None, prepare=
                  _stream(residual))
 
 
+def dit_modulate_scale_shift(x, scale, shift, mode="lossless", out=None, prepare=False):
+    """bf(bf(x * bf(1 + scale)) + shift) with modulation row r // (rows // mod_rows)."""
+    _same_device(x, scale, shift)
+    rows, x_rs = _flat_rows(x, "x")
+    dim = x.shape[-1]
+    mrows, mrs = _mod_rows(scale, shift, dim, ("scale", "shift"))
+    out = _out_like(x, out)
+    _same_device(x, out)
+    _, o_rs = _flat_rows(out, "out")
+    return _call("dit_modulate_scale_shift", out, prepare, out.data_ptr(), o_rs, x.data_ptr(),
+                 x_rs, scale.data_ptr(), shift.data_ptr(), mrs, mrows, rows, dim, _mode(mode),
+                 _stream(x))
+
+
 def dit_gate_add_ln_modulate(residual, y, gate, scale, shift, eps=1e-6, mode="lossless",
                              out_residual=None, out=None, prepare=False):
     """r' = bf(residual + bf(gate * y)) and LN(r') * (1 + scale) + shift in one
@@ -431,6 +450,41 @@ def dit_qk_norm_rope(txt, img, cos, sin, eps=1e-6, mode="lossless", out=None, pr
     return _call("dit_qk_norm_rope", out, prepare, qo.data_ptr(), ko.data_ptr(), vo.data_ptr(),
                  qo.stride(1), qo.stride(0), ctypes.pointer(ts), ctypes.pointer(is_),
                  cos.data_ptr(), sin.data_ptr(), B, H, Dh, eps, _mode(mode), _stream(ref))
+
+
+def dit_qk_norm_rope_packed(txt, img, cos, sin, dests, eps=1e-6, mode="lossless", out=None,
+                            prepare=False):
+    """The QKV epilogue written destination-major for Ulysses: returns the
+    contiguous bfloat16 buffer [P, B, S_txt + S_img, 3, H / P, Dh] (P = dests)
+    whose chunk p holds heads p H/P .. (p + 1) H/P - 1 of q, k and v, ready for
+    one all-to-all.  ``out`` may be such a buffer."""
+    ts, tshape = _qkv_stream(txt)
+    is_, ishape = _qkv_stream(img)
+    ref = img["q"] if img is not None else txt["q"]
+    B, _, H, Dh = ref.shape
+    s_total = ts.tokens + is_.tokens
+    if dests <= 0 or H % dests:
+        raise DitInvalid(f"dests={dests} must divide heads={H}")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32 or not cos.is_contiguous() \
+            or not sin.is_contiguous():
+        raise DitUnsupported("cos and sin must be contiguous float32 tensors")
+    if cos.shape != (s_total, Dh // 2) or sin.shape != (s_total, Dh // 2):
+        raise DitInvalid(f"cos/sin must be [{s_total}, {Dh // 2}]")
+    for sh in (tshape, ishape):
+        if sh[0] and (sh[0] != B or sh[2] != H or sh[3] != Dh):
+            raise DitInvalid("text and image streams must agree on batch, heads and head_dim")
+    hpd = H // dests
+    shape = (dests, B, s_total, 3, hpd, Dh)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=ref.device)
+    if tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise DitInvalid(f"out must be a contiguous bfloat16 {list(shape)} buffer")
+    base, esz = out.data_ptr(), out.element_size()
+    ts_out = 3 * hpd * Dh
+    return _call("dit_qk_norm_rope_dest", out, prepare, base, base + hpd * Dh * esz,
+                 base + 2 * hpd * Dh * esz, ts_out, s_total * ts_out, hpd,
+                 B * s_total * ts_out, ctypes.pointer(ts), ctypes.pointer(is_), cos.data_ptr(),
+                 sin.data_ptr(), B, H, Dh, eps, _mode(mode), _stream(ref))
 
 
 def dit_time_next_launch(start, stop):

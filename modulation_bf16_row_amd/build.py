@@ -21,8 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 
-SOURCES = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_qkv.hip",
-           "dit_modtab.hip", "dit_probe.hip", "dit_abi.cpp"]
+SOURCES = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_mod.hip",
+           "dit_qkv.hip", "dit_modtab.hip", "dit_probe.hip", "dit_abi.cpp"]
 
 ARCH = "gfx950"
 COMMON = [

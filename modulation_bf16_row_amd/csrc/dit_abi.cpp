@@ -242,6 +242,27 @@ dit_status_t dit_residual_gate_add(void *out, int64_t out_rs, const void *residu
   return hip_status(dit::launch_residual_gate_add(a, stream));
 }
 
+dit_status_t dit_modulate_scale_shift(void *out, int64_t out_rs, const void *x, int64_t x_rs,
+                                      const void *scale, const void *shift, int64_t mod_rs,
+                                      int64_t mod_rows, int64_t rows, int64_t dim, int mode,
+                                      hipStream_t stream) {
+  const RowProblem p{rows, dim, mod_rows, mode};
+  DIT_TRY(check_shape(p, true));
+  if (rows == 0) return DIT_OK;
+  DIT_TRY(check_rows(out, out_rs, rows, dim, "out is NULL", "bad out row stride"));
+  DIT_TRY(check_rows(x, x_rs, rows, dim, "x is NULL", "bad x row stride"));
+  DIT_TRY(check_rows(scale, mod_rs, mod_rows, dim, "scale is NULL", "bad modulation row stride"));
+  DIT_TRY(check_rows(shift, mod_rs, mod_rows, dim, "shift is NULL", "bad modulation row stride"));
+  const Span so = rows_span(out, out_rs, rows, dim);
+  const Span ins[] = {rows_span(x, x_rs, rows, dim)};
+  const Span cs[] = {rows_span(scale, mod_rs, mod_rows, dim),
+                     rows_span(shift, mod_rs, mod_rows, dim)};
+  DIT_TRY(check_out_alias(so, ins, 1, cs, 2));
+  dit::ModArgs a{static_cast<uint16_t *>(out), u16(x), u16(scale), u16(shift), out_rs, x_rs,
+                 mod_rs, rows, dim, rows / mod_rows};
+  return hip_status(dit::launch_modulate_scale_shift(a, stream));
+}
+
 dit_status_t dit_gate_add_ln_modulate(void *out_residual, int64_t out_res_rs, void *out,
                                       int64_t out_rs, const void *residual, int64_t res_rs,
                                       const void *y, int64_t y_rs, const void *gate,
@@ -401,14 +422,53 @@ dit_status_t dit_gate_add_ln_modulate_fp8(
 
 namespace {
 
-// Segments of a [batch, tokens, heads*128] view with the given strides.
+// Up to three (stride, count) levels of a strided view whose innermost
+// runs are `width` elements: segment offsets sum_i k_i * stride_i, k_i <
+// count_i.  Levels with one entry or stride 0 add no segments.
+struct Lattice {
+  int64_t stride[3], count[3];
+};
+
+// The view's segments as one Span: exact-or-wider (step = the smallest
+// stride, every multiple of it up to the last offset) when each stride is a
+// multiple of the smallest, else one segment covering the hull.
+Span lattice_span(const void *p, const Lattice &l, int64_t width) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  int64_t inner = 0, last = 0;
+  for (int i = 0; i < 3; ++i)
+    if (l.count[i] > 1 && l.stride[i] > 0) {
+      last += (l.count[i] - 1) * l.stride[i];
+      if (inner == 0 || l.stride[i] < inner) inner = l.stride[i];
+    }
+  if (inner == 0) return Span{base, 0, 1, width * 2};
+  for (int i = 0; i < 3; ++i)
+    if (l.count[i] > 1 && l.stride[i] > 0 && l.stride[i] % inner != 0)
+      return Span{base, 0, 1, (last + width) * 2};
+  return Span{base, inner * 2, last / inner + 1, width * 2};
+}
+
+// True when the view's segments are pairwise disjoint because its levels
+// nest: in increasing stride order each stride is at least the extent of
+// everything inside it.  (A sufficient test; layouts whose levels
+// interleave are rejected.)
+bool lattice_disjoint(const Lattice &l, int64_t width) {
+  int idx[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (l.stride[idx[j]] < l.stride[idx[i]]) std::swap(idx[i], idx[j]);
+  int64_t extent = width;
+  for (int i : idx) {
+    if (l.count[i] <= 1) continue;
+    if (l.stride[i] < extent) return false;
+    extent += (l.count[i] - 1) * l.stride[i];
+  }
+  return true;
+}
+
+// Segments of a [batch, tokens, w] view with token stride ts and batch stride bs.
 Span token_span(const void *p, int64_t ts, int64_t bs, int64_t batch, int64_t tokens,
                 int64_t width) {
-  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
-  if (batch <= 1 || (ts > 0 && bs % ts == 0 && bs >= tokens * ts))
-    return Span{base, ts * 2, (batch <= 1 ? 0 : (batch - 1) * (ts > 0 ? bs / ts : 0)) + tokens,
-                width * 2};
-  return Span{base, 0, 1, ((batch - 1) * bs + (tokens - 1) * ts + width) * 2};
+  return lattice_span(p, Lattice{{ts, bs, 0}, {tokens, batch, 1}}, width);
 }
 
 dit_status_t check_stream(const dit_qkv_stream_t *st, int64_t batch, int64_t width) {
@@ -428,14 +488,11 @@ dit_status_t check_stream(const dit_qkv_stream_t *st, int64_t batch, int64_t wid
   return DIT_OK;
 }
 
-}  // namespace
-
-extern "C" dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out,
-                                         int64_t out_tok_stride, int64_t out_batch_stride,
-                                         const dit_qkv_stream_t *txt, const dit_qkv_stream_t *img,
-                                         const float *cos, const float *sin, int64_t batch,
-                                         int64_t heads, int64_t head_dim, float eps, int mode,
-                                         hipStream_t stream) {
+dit_status_t qkv_impl(void *q_out, void *k_out, void *v_out, int64_t out_tok_stride,
+                      int64_t out_batch_stride, int64_t heads_per_dest, int64_t dest_stride,
+                      const dit_qkv_stream_t *txt, const dit_qkv_stream_t *img, const float *cos,
+                      const float *sin, int64_t batch, int64_t heads, int64_t head_dim, float eps,
+                      int mode, hipStream_t stream) {
   if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
     return fail(DIT_ERR_INVALID, "unknown mode");
   if (batch < 0 || heads < 0 || head_dim < 0) return fail(DIT_ERR_INVALID, "negative size");
@@ -448,24 +505,32 @@ extern "C" dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out,
   if (batch == 0 || heads == 0 || s_total == 0) return DIT_OK;
   if (head_dim != DIT_QK_HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "head_dim != 128");
   if (heads > 64) return fail(DIT_ERR_UNSUPPORTED, "heads > 64");
-  const int64_t width = heads * head_dim;
+  if (heads_per_dest <= 0 || heads % heads_per_dest != 0)
+    return fail(DIT_ERR_INVALID, "heads_per_dest must divide heads");
+  const int64_t dests = heads / heads_per_dest;
+  if (dest_stride < 0) return fail(DIT_ERR_INVALID, "negative destination stride");
+  if (dests > 1 && dest_stride % 8 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "destination stride % 8 != 0");
+  const int64_t width = heads * head_dim;         // one token of an input stream
+  const int64_t dwidth = heads_per_dest * head_dim;  // one token of one destination
   DIT_TRY(check_stream(st_txt, batch, width));
   DIT_TRY(check_stream(st_img, batch, width));
   if (!q_out || !k_out || !v_out || !cos || !sin)
     return fail(DIT_ERR_INVALID, "output or table pointer is NULL");
   if (out_tok_stride < 0 || out_batch_stride < 0)
     return fail(DIT_ERR_INVALID, "negative output stride");
-  if ((s_total > 1 && out_tok_stride < width) || out_tok_stride % 8 != 0 ||
-      (batch > 1 && (out_batch_stride % 8 != 0 || out_batch_stride < width)))
+  if (out_tok_stride % 8 != 0 || out_batch_stride % 8 != 0)
     return fail(DIT_ERR_UNSUPPORTED, "output strides");
+  const Lattice lo{{out_tok_stride, out_batch_stride, dest_stride}, {s_total, batch, dests}};
+  if (!lattice_disjoint(lo, dwidth))
+    return fail(DIT_ERR_UNSUPPORTED, "output strides make an output overlap itself");
   const void *ps[] = {q_out, k_out, v_out, cos, sin};
   for (const void *p : ps)
     if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "pointer is not 16-byte aligned");
   if ((batch * s_total + 3) / 4 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
 
-  const Span outs[3] = {token_span(q_out, out_tok_stride, out_batch_stride, batch, s_total, width),
-                        token_span(k_out, out_tok_stride, out_batch_stride, batch, s_total, width),
-                        token_span(v_out, out_tok_stride, out_batch_stride, batch, s_total, width)};
+  const Span outs[3] = {lattice_span(q_out, lo, dwidth), lattice_span(k_out, lo, dwidth),
+                        lattice_span(v_out, lo, dwidth)};
   for (int i = 0; i < 3; ++i)
     for (int j = i + 1; j < 3; ++j)
       if (spans_overlap(outs[i], outs[j]))
@@ -509,8 +574,34 @@ extern "C" dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out,
   a.batch = batch;
   a.heads = heads;
   a.s_total = s_total;
+  a.heads_per_dest = heads_per_dest;
+  a.dest_stride = dests > 1 ? dest_stride : 0;
   a.eps = eps;
   return hip_status(dit::launch_qk_norm_rope(a, mode, stream));
+}
+
+}  // namespace
+
+extern "C" dit_status_t dit_qk_norm_rope(void *q_out, void *k_out, void *v_out,
+                                         int64_t out_tok_stride, int64_t out_batch_stride,
+                                         const dit_qkv_stream_t *txt, const dit_qkv_stream_t *img,
+                                         const float *cos, const float *sin, int64_t batch,
+                                         int64_t heads, int64_t head_dim, float eps, int mode,
+                                         hipStream_t stream) {
+  return qkv_impl(q_out, k_out, v_out, out_tok_stride, out_batch_stride, heads > 0 ? heads : 1, 0,
+                  txt, img, cos, sin, batch, heads, head_dim, eps, mode, stream);
+}
+
+extern "C" dit_status_t dit_qk_norm_rope_dest(void *q_out, void *k_out, void *v_out,
+                                              int64_t out_tok_stride, int64_t out_batch_stride,
+                                              int64_t heads_per_dest, int64_t dest_stride,
+                                              const dit_qkv_stream_t *txt,
+                                              const dit_qkv_stream_t *img, const float *cos,
+                                              const float *sin, int64_t batch, int64_t heads,
+                                              int64_t head_dim, float eps, int mode,
+                                              hipStream_t stream) {
+  return qkv_impl(q_out, k_out, v_out, out_tok_stride, out_batch_stride, heads_per_dest,
+                  dest_stride, txt, img, cos, sin, batch, heads, head_dim, eps, mode, stream);
 }
 
 // ---------------------------------------------------------------------------

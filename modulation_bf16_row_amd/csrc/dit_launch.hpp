@@ -81,6 +81,15 @@ struct GateAddArgs {
   int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
+struct ModArgs {
+  uint16_t *out;
+  const uint16_t *x, *scale, *shift;
+  int64_t out_rs, x_rs, mod_rs;
+  int64_t rows, dim, per_mod;
+  int64_t rows_per_wave;       // set by the launcher
+  int64_t blocks_per_mod;      // set by the launcher (staged layout)
+};
+
 struct QkvStreamArgs {
   const uint16_t *q, *k, *v;
   const uint16_t *q_weight, *k_weight;
@@ -94,6 +103,9 @@ struct QkvArgs {
   QkvStreamArgs txt, img;
   const float *cos, *sin;
   int64_t batch, heads, s_total;
+  // Head h is written at (h / heads_per_dest) * dest_stride + (h % heads_per_dest) * 128
+  // within its token's output row (heads_per_dest = heads: plain joint layout).
+  int64_t heads_per_dest, dest_stride;
   float eps;
   int64_t tokens_per_wave;     // set by the launcher
   int64_t parts;               // set by the launcher: waves sharing one token's heads
@@ -112,6 +124,7 @@ hipError_t launch_gate_add_ln_modulate(const GateLnArgs &a, int mode, hipStream_
 hipError_t launch_rmsnorm_scale(const RmsScaleArgs &a, int mode, hipStream_t s);
 hipError_t launch_rmsnorm_tanh_residual(const RmsTanhArgs &a, int mode, hipStream_t s);
 hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t s);
+hipError_t launch_modulate_scale_shift(const ModArgs &a, hipStream_t s);
 hipError_t launch_qk_norm_rope(const QkvArgs &a, int mode, hipStream_t s);
 
 // Device-primitive probes (exhaustive tests of the kernels' own helpers).

@@ -12,6 +12,13 @@
 // cos/sin loaded once per token and part and reused for every head.
 // Splitting a token over several waves trades a few repeated cos/sin and
 // weight reads (cache hits) for fewer VGPRs per wave and more waves.
+//
+// Output placement: head h lands at (h / hpd) * dest_stride + (h % hpd) * 128
+// of its token's output row.  hpd = heads gives the joint [B, S, H, 128]
+// layout; hpd = H / P with dest_stride = the size of one destination's block
+// writes the destination-major buffer whose P contiguous chunks an
+// all-to-all hands one to each rank under Ulysses sequence parallelism (page
+// "基于Agent的SGLang扩散模型Kernel优化实践", section "Ulysses QKV仅执行一次All-to-All").
 #include <stdlib.h>
 
 #include "dit_device.hpp"
@@ -110,6 +117,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int g = lane >> 4;           // head within the group of four
   const int r = lane & 15;           // 8-element slice of the head
 
+  // Output offset of each of the wave's heads within a token's row: its
+  // destination's block, then its position there.
+  int64_t ho[HG];
+#pragma unroll
+  for (int i = 0; i < HG; ++i) {
+    const int h = 4 * (g0 + i) + g;
+    const int hpd = (int)a.heads_per_dest;
+    ho[i] = (int64_t)(h / hpd) * a.dest_stride + (int64_t)(h % hpd) * kHeadDim;
+  }
+
   for (int64_t t = t0; t < t1; ++t) {
     Token<HG> cur;
     load_token<HG>(cur, a, t, g0, g, r);
@@ -119,11 +136,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
       // Lanes of absent heads (h >= heads) fill whole 16-lane groups of
       // their own, so the group sums of present heads never read them.
       if (h < a.heads) {
-        store8(a.v_out + cur.dst + h * kHeadDim, cur.v[i]);
-        store8(a.q_out + cur.dst + h * kHeadDim, norm_rope<MODE>(cur.q[i], cur.wq, cur.c, cur.z,
-                                                                 a.eps));
-        store8(a.k_out + cur.dst + h * kHeadDim, norm_rope<MODE>(cur.k[i], cur.wk, cur.c, cur.z,
-                                                                 a.eps));
+        store8(a.v_out + cur.dst + ho[i], cur.v[i]);
+        store8(a.q_out + cur.dst + ho[i], norm_rope<MODE>(cur.q[i], cur.wq, cur.c, cur.z, a.eps));
+        store8(a.k_out + cur.dst + ho[i], norm_rope<MODE>(cur.k[i], cur.wk, cur.c, cur.z, a.eps));
       }
     }
   }

@@ -48,9 +48,9 @@ constexpr int kThreads = 64 * kWavesPerBlock;
 // (Qwen-Image and Wan shapes): the nontemporal policy helps the kernels that
 // read two or more row streams and slows the single-stream norms.
 #ifdef DIT_NO_NT_LOAD
-constexpr bool kNtLn = false, kNtRms = false, kNtTanh = false, kNtGate = false;
+constexpr bool kNtLn = false, kNtRms = false, kNtTanh = false, kNtGate = false, kNtMod = false;
 #else
-constexpr bool kNtLn = false, kNtRms = false, kNtTanh = true, kNtGate = true;
+constexpr bool kNtLn = false, kNtRms = false, kNtTanh = true, kNtGate = true, kNtMod = false;
 #endif
 
 // Register budget: at least W6 waves per SIMD at dim <= 3072 (NC <= 6),

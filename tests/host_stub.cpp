@@ -56,9 +56,16 @@ hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t) {
 }
 
 hipError_t launch_qk_norm_rope(const QkvArgs &a, int mode, hipStream_t) {
-  const int64_t v[] = {a.batch, a.heads, a.s_total, a.out_ts, a.out_bs, a.txt.tokens,
-                       a.img.tokens, a.txt.tok_stride, a.img.tok_stride};
-  rec("qk_norm_rope", mode, v, 9);
+  const int64_t v[] = {a.batch,       a.heads,          a.s_total,         a.out_ts,
+                       a.out_bs,      a.txt.tokens,     a.img.tokens,      a.txt.tok_stride,
+                       a.img.tok_stride, a.heads_per_dest, a.dest_stride};
+  rec("qk_norm_rope", mode, v, 11);
+  return hipSuccess;
+}
+
+hipError_t launch_modulate_scale_shift(const ModArgs &a, hipStream_t) {
+  const int64_t v[] = {a.rows, a.dim, a.per_mod, a.out_rs, a.x_rs, a.mod_rs};
+  rec("modulate_scale_shift", 0, v, 6);
   return hipSuccess;
 }
 

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     lib.dit_abi_version.restype = cint
-    assert lib.dit_abi_version() == 2
+    assert lib.dit_abi_version() == 3
 
 
 @pytest.fixture(scope="module")
@@ -335,3 +335,112 @@ def test_qkv_guards(stub):
     # misaligned table
     assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
                 cos=A * 40 + 4) == UNSUPPORTED
+
+
+def test_qkv_rejects_outputs_that_overlap_themselves(stub):
+    r = Rec(stub)
+    txt, img = _streams()
+    H, Dh, S, B = 24, 128, 4608, 2
+    base = A * 512
+    sep = A * 64
+    # batch stride = token stride: batch 1 token 0 would be batch 0 token 1
+    n0 = r.calls
+    assert _qkv(stub, txt, img, base, base + sep, base + 2 * sep, H * Dh, H * Dh) == UNSUPPORTED
+    assert "overlap itself" in stub.dit_status_reason().decode()
+    # token stride below a token's width
+    assert _qkv(stub, txt, img, base, base + sep, base + 2 * sep, H * Dh - 8, S * H * Dh) \
+        == UNSUPPORTED
+    assert r.calls == n0
+    # token-major [S, B, H, Dh] nests the other way round and is accepted
+    assert _qkv(stub, txt, img, base, base + sep, base + 2 * sep, B * H * Dh, H * Dh) == OK
+    # one token: the token stride is never used
+    one = Stream(txt.q, txt.k, txt.v, txt.tok_stride, txt.batch_stride, txt.q_weight,
+                 txt.k_weight, 1)
+    assert _qkv(stub, one, None, base, base + sep, base + 2 * sep, 0, H * Dh) == OK
+
+
+def _qkv_dest(lib, txt, img, qo, ko, vo, ots, obs, hpd, ds, batch=2, heads=24, mode=0):
+    lib.dit_qk_norm_rope_dest.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(Stream),
+                                          ctypes.POINTER(Stream), vp, vp, i64, i64, i64, f32,
+                                          cint, vp]
+    return lib.dit_qk_norm_rope_dest(qo, ko, vo, ots, obs, hpd, ds,
+                                     ctypes.byref(txt) if txt else None,
+                                     ctypes.byref(img) if img else None, A * 40, A * 44, batch,
+                                     heads, 128, 1e-6, mode, None)
+
+
+def test_qkv_destination_major_guards(stub):
+    r = Rec(stub)
+    txt, img = _streams()
+    H, Dh, S, B = 24, 128, 4608, 2
+    base = A * 512
+    for P in (1, 2, 4, 8):
+        hpd = H // P
+        ts = 3 * hpd * Dh
+        bs, ds = S * ts, B * S * ts
+        assert _qkv_dest(stub, txt, img, base, base + 2 * hpd * Dh, base + 4 * hpd * Dh, ts, bs,
+                         hpd, ds) == OK
+        assert r.name == "qk_norm_rope"
+        assert r.vals[:5] == [B, H, S, ts, bs]
+        assert r.vals[9:11] == [hpd, ds if P > 1 else 0]
+    # the plain entry point forwards a single destination
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh) == OK
+    assert r.vals[9:11] == [H, 0]
+    hpd, ts = 6, 3 * 6 * Dh
+    bs, ds = S * ts, B * S * ts
+    n0 = r.calls
+    for kw, status, why in [
+            (dict(hpd=5), INVALID, "heads_per_dest"),
+            (dict(hpd=0), INVALID, "heads_per_dest"),
+            (dict(ds=-8), INVALID, "negative destination"),
+            (dict(ds=ds + 4), UNSUPPORTED, "% 8"),
+            (dict(ds=bs), UNSUPPORTED, "overlap itself"),            # destinations collide
+            (dict(ds=ds - 8), INVALID, "overlap each other"),        # q of p+1 over v of p
+            (dict(ots=hpd * Dh - 8), UNSUPPORTED, "overlap itself"),
+            (dict(ko=base + 2 * (hpd * Dh - 8)), INVALID, "overlap each other"),
+            (dict(qo=txt.q), INVALID, "overlaps an input"),
+    ]:
+        args = dict(qo=base, ko=base + 2 * hpd * Dh, vo=base + 4 * hpd * Dh, ots=ts, obs=bs,
+                    hpd=hpd, ds=ds)
+        args.update(kw)
+        assert _qkv_dest(stub, txt, img, **args) == status, kw
+        assert why.lower() in stub.dit_status_reason().decode().lower(), kw
+    assert r.calls == n0
+    # destinations interleaved per token ([B, S, P, 3, hpd, Dh]) also nest
+    assert _qkv_dest(stub, txt, img, base, base + 2 * hpd * Dh, base + 4 * hpd * Dh, 4 * ts,
+                     S * 4 * ts, hpd, ts) == OK
+
+
+def mod(lib, out=OUT, out_rs=512, x=X, x_rs=512, sc=SC, sh=SH, mod_rs=512, mod_rows=2, rows=8,
+        dim=512, mode=0):
+    lib.dit_modulate_scale_shift.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, cint,
+                                             vp]
+    return lib.dit_modulate_scale_shift(out, out_rs, x, x_rs, sc, sh, mod_rs, mod_rows, rows, dim,
+                                        mode, None)
+
+
+def test_modulate_scale_shift_guards(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert mod(stub, x_rs=1024, out_rs=2048) == OK
+    assert r.calls == n0 + 1 and r.name == "modulate_scale_shift"
+    assert r.vals[:6] == [8, 512, 4, 2048, 1024, 512]
+    assert mod(stub, out=X) == OK                                # in place
+    assert mod(stub, mode=1) == OK
+    assert mod(stub, rows=0, x=0, out=0) == OK
+    n1 = r.calls
+    for kw, status, why in [
+            (dict(out=X + 16), INVALID, "partially overlaps"),
+            (dict(out=SC), INVALID, "modulation"),
+            (dict(out=SH + 512), INVALID, "modulation"),
+            (dict(sh=0), INVALID, "shift is NULL"),
+            (dict(mod_rows=3), UNSUPPORTED, "mod_rows"),
+            (dict(dim=508, x_rs=512), UNSUPPORTED, "% 8"),
+            (dict(dim=8200, x_rs=8200, out_rs=8200, mod_rs=8200), UNSUPPORTED, "8192"),
+            (dict(x_rs=500), UNSUPPORTED, "stride"),
+            (dict(x=X + 2), UNSUPPORTED, "aligned"),
+            (dict(mode=5), INVALID, "mode"),
+    ]:
+        assert mod(stub, **kw) == status, kw
+        assert why.lower() in stub.dit_status_reason().decode().lower(), kw
+    assert r.calls == n1
