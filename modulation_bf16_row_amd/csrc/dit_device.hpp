@@ -65,6 +65,7 @@ __device__ __forceinline__ float round_f64(double v) {
 //   m = 8:    DPP row_ror:8 (lane i of a row reads lane (i + 8) mod 16);
 //   m = 16:   ds_swizzle, bit mode: and 0x1F, or 0, xor 0x10;
 //   m = 32:   ds_bpermute.
+// (wave_sum takes its last two stages from row_pair_add / half_pair_add.)
 __device__ __forceinline__ float partner(float p, int m) {
   const int v = __float_as_int(p);
   int r;
@@ -84,14 +85,32 @@ __device__ __forceinline__ float partner(float p, int m) {
 
 __device__ __forceinline__ float xor_add(float p, int m) { return p + partner(p, m); }
 
+// Stages m = 16 and m = 32 of the tree once every row of 16 lanes (for 16),
+// or every half of 32 lanes (for 32), holds a single value: the gfx950 swaps
+// v_permlane16_swap (rows 0 <-> 1 and 2 <-> 3) and v_permlane32_swap
+// (lanes 0-31 <-> 32-63) hand each lane its partner row's (half's) value
+// through the VALU, without the LDS round trip of ds_swizzle/ds_bpermute.
+// The swapped pair sums to p_a + p_b, the same bits as the xor partner.
+__device__ __forceinline__ float row_pair_add(float p) {
+  const uint32_t u = __float_as_uint(p);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float half_pair_add(float p) {
+  const uint32_t u = __float_as_uint(p);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // All 64 lanes: m = 1, 2, 4, 8, 16, 32.
 __device__ __forceinline__ float wave_sum(float p) {
   p = xor_add(p, 1);
   p = xor_add(p, 2);
   p = xor_add(p, 4);
   p = xor_add(p, 8);
-  p = xor_add(p, 16);
-  p = xor_add(p, 32);
+  p = row_pair_add(p);     // m = 16
+  p = half_pair_add(p);    // m = 32
   return p;
 }
 
