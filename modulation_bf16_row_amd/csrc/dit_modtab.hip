@@ -5,48 +5,91 @@
 // and the per-token time embedding, stored directly in (6, B, S, D) layout
 // instead of strided chunks of a temporary, with the same addition).
 //
-// Geometry: output row r = (k, token) of D floats, one 512-thread workgroup
-// per row (grid-stride beyond 2^31 - 1 rows); the threads cover the row's
-// 4-element groups: per group an 8-byte nontemporal load of 4 bf16
-// time-embedding values, a 16-byte load of the table (default policy: the
-// table, n_mod * D * 4 bytes, stays cached) and one 16-byte nontemporal
-// store, so every wave instruction moves a contiguous span (512 bytes in,
-// 1 KiB out) and each store fills whole cache lines.  Pure streaming: 6
-// bytes of HBM traffic per output element.  At the Wan 720p shape (6 x
-// 75600 x 5120) this measured 2.75 ms against 2.91 ms for 256-thread
-// workgroups striding over 55 rows each, 2.83 ms with eight rows' loads in
-// flight per thread, and 2.79 ms token-major (a token's six chunks per
-// workgroup).
+// Geometry: the output, viewed as groups of 4 consecutive floats in output
+// order, is covered one group per lane by 64-thread workgroups (one wave
+// each).  A lane makes one 8-byte nontemporal load of 4 bf16 time-embedding
+// values, one 16-byte load of the table (default policy: the table,
+// n_mod * D * 4 bytes, stays cached) and one 16-byte nontemporal store.
+// Pure streaming, 6 bytes of HBM traffic per output element.  Small
+// one-shot workgroups stream best on MI355X: at the Wan 720p shape (6 x
+// 75600 x 5120) this layout measured 2.35 ms against 2.49, 2.56 and 2.72 ms
+// for 128-, 256- and 512-thread workgroups of the same layout, 2.74 ms for
+// one 512-thread workgroup per output row, and 3.13 ms with 8 outputs per
+// lane.
+//
+// Index arithmetic: a lane's group g splits into output row r = g / (D/4)
+// and row r into chunk k = r / (B*S) and token t.  While every group index
+// fits 32 bits, both quotients are exact multiply-high products with a
+// reciprocal computed on the host (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994): for 2 <= d < 2^32
+// and M = floor(2^64 / d) + 1, the error term n * (M d - 2^64) < 2^64 for
+// every n < 2^32, so floor(n M / 2^64) = floor(n / d).  Larger problems
+// take a grid-stride loop with 64-bit division.
 #include "dit_device.hpp"
 #include "dit_launch.hpp"
 
 namespace dit {
 
-constexpr int kModtabThreads = 512;
+constexpr int kModtabThreads = 64;
 
-__global__ __launch_bounds__(kModtabThreads) void k_wan_mod_table(ModTableArgs a) {
-  const int64_t tokens = a.batch * a.tokens;          // rows per modulation chunk
-  const int64_t rows = a.n_mod * tokens;
-  const int ng = (int)(a.dim / 4);
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const int64_t k = r / tokens, t = r - k * tokens;
-    const uint16_t *e = a.temb + (t * a.n_mod + k) * a.dim;
-    const float *tb = a.table + k * a.dim;
-    float *o = a.out + r * a.dim;
-    for (int g = threadIdx.x; g < ng; g += kModtabThreads) {
-      const u32x2 ev = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(e + 4 * g));
-      const float4 tv = *reinterpret_cast<const float4 *>(tb + 4 * g);
-      const u32x4 ov = {__float_as_uint(tv.x + lo(ev[0])), __float_as_uint(tv.y + hi(ev[0])),
-                        __float_as_uint(tv.z + lo(ev[1])), __float_as_uint(tv.w + hi(ev[1]))};
-      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4 *>(o + 4 * g));
-    }
+// floor(n / d) from M = floor(2^64 / d) + 1; M == 0 stands for d == 1.
+__device__ __forceinline__ uint32_t div_by(uint32_t n, uint64_t m) {
+  return m ? (uint32_t)__umul64hi((uint64_t)n, m) : n;
+}
+
+// Output group gi (4 floats) of row (k, t): table[k] + temb[t][k].
+__device__ __forceinline__ void table_group(const ModTableArgs &a, uint64_t k, uint64_t t,
+                                            uint64_t gi, uint64_t g) {
+  const u32x2 ev = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x2 *>(a.temb + (t * a.n_mod + k) * a.dim + 4 * gi));
+  const float4 tv = *reinterpret_cast<const float4 *>(a.table + k * a.dim + 4 * gi);
+  const u32x4 ov = {__float_as_uint(tv.x + lo(ev[0])), __float_as_uint(tv.y + hi(ev[0])),
+                    __float_as_uint(tv.z + lo(ev[1])), __float_as_uint(tv.w + hi(ev[1]))};
+  __builtin_nontemporal_store(ov, reinterpret_cast<u32x4 *>(a.out + 4 * g));
+}
+
+// 32-bit indices: one group per lane, every group index < 2^32.
+__global__ __launch_bounds__(kModtabThreads) void k_wan_mod_table(ModTableArgs a, uint32_t groups,
+                                                                 uint64_t m_row, uint64_t m_tok) {
+  const uint32_t g = blockIdx.x * kModtabThreads + threadIdx.x;
+  if (g >= groups) return;
+  const uint32_t gpr = (uint32_t)(a.dim / 4), tokens = (uint32_t)(a.batch * a.tokens);
+  const uint32_t r = div_by(g, m_row), gi = g - r * gpr;
+  const uint32_t k = div_by(r, m_tok), t = r - k * tokens;
+  table_group(a, k, t, gi, g);
+}
+
+// 64-bit indices, grid-stride.
+__global__ __launch_bounds__(kModtabThreads) void k_wan_mod_table_wide(ModTableArgs a) {
+  const uint64_t gpr = (uint64_t)a.dim / 4, tokens = (uint64_t)(a.batch * a.tokens);
+  const uint64_t groups = (uint64_t)a.n_mod * tokens * gpr;
+  const uint64_t step = (uint64_t)gridDim.x * kModtabThreads;
+  for (uint64_t g = (uint64_t)blockIdx.x * kModtabThreads + threadIdx.x; g < groups; g += step) {
+    const uint64_t r = g / gpr, gi = g - r * gpr;
+    const uint64_t k = r / tokens, t = r - k * tokens;
+    table_group(a, k, t, gi, g);
   }
 }
 
+// floor(2^64 / d) + 1 for 2 <= d < 2^32, 0 for d == 1.
+static uint64_t reciprocal(uint64_t d) {
+  if (d < 2) return 0;
+  const uint64_t q = ~0ull / d, rem = ~0ull % d;     // 2^64 - 1 = q d + rem
+  return q + (rem == d - 1 ? 1 : 0) + 1;             // d | 2^64 exactly when rem == d - 1
+}
+
 hipError_t launch_wan_mod_table(const ModTableArgs &a, hipStream_t s) {
-  const int64_t rows = a.n_mod * a.batch * a.tokens;
-  const dim3 grid((unsigned)(rows < 0x7FFFFFFF ? rows : 0x7FFFFFFF));
-  DIT_LAUNCH(k_wan_mod_table, grid, dim3(kModtabThreads), 0, s, a);
+  const uint64_t tokens = (uint64_t)(a.batch * a.tokens);
+  const uint64_t groups = (uint64_t)a.n_mod * tokens * (uint64_t)(a.dim / 4);
+  if (groups < (1ull << 32)) {
+    const dim3 grid((unsigned)((groups + kModtabThreads - 1) / kModtabThreads));
+    DIT_LAUNCH(k_wan_mod_table, grid, dim3(kModtabThreads), 0, s, a, (uint32_t)groups,
+               reciprocal((uint64_t)(a.dim / 4)), reciprocal(tokens));
+  } else {
+    const uint64_t blocks = (groups + kModtabThreads - 1) / kModtabThreads;
+    const dim3 grid((unsigned)(blocks < 0x7FFFFFFF ? blocks : 0x7FFFFFFF));
+    DIT_LAUNCH(k_wan_mod_table_wide, grid, dim3(kModtabThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

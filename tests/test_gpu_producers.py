@@ -261,7 +261,8 @@ def test_fp8_qwen_block_full_size():
 # --------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,S,K,D", [(1, 1, 6, 8), (1, 37, 6, 520), (2, 100, 6, 3072),
-                                     (1, 300, 6, 5120), (3, 7, 2, 1032)])
+                                     (1, 300, 6, 5120), (3, 7, 2, 1032), (2, 64, 6, 1024),
+                                     (1, 2, 1, 16)])
 def test_wan_modulation_table_shapes(B, S, K, D):
     say("wan modulation table", B, S, K, D)
     rng = np.random.default_rng(B * 1000 + S + D)
@@ -293,3 +294,30 @@ def test_wan_modulation_table_full_size():
     ref = oracle.wan_mod_table(t_h, e_h)
     got = out.index_select(2, tok).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_wan_modulation_table_beyond_32_bit_indices():
+    """6 x 2^20 tokens x 2736: 4.30e9 groups of four outputs, past 2^32, so the
+    launch takes the 64-bit grid-stride kernel (69 GB out, 34 GB in, drawn on
+    the device in slices).  Chunk k = 5, which holds the groups past 2^32,
+    against torch's binary32 addition on every element; sampled tokens of
+    every chunk against the oracle."""
+    S, K, D = 1 << 20, 6, 2736
+    say("wan modulation table beyond 2^32 groups [1, %d, %d, %d]" % (S, K, D))
+    g = torch.Generator(device="cuda").manual_seed(4200)
+    table = torch.randn((K, D), device="cuda", generator=g) * 0.05
+    temb = torch.empty((1, S, K, D), dtype=torch.bfloat16, device="cuda")
+    step = 1 << 16
+    for s0 in range(0, S, step):
+        temb[:, s0:s0 + step] = (torch.randn((1, step, K, D), device="cuda", generator=g)
+                                 * 0.3).to(torch.bfloat16)
+    out = m().dit_wan_modulation_table(table, temb)
+    ref = table[K - 1][None, None, :] + temb[:, :, K - 1, :].float()
+    assert torch.equal(out[K - 1].view(torch.int32), ref.view(torch.int32))
+    del ref
+    tok = torch.tensor([0, 1, (1 << 19) + 3, S - 2, S - 1], device="cuda")
+    ref = oracle.wan_mod_table(table.cpu().numpy(), host(temb.index_select(1, tok)))
+    got = out.index_select(2, tok).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    del out, temb
+    torch.cuda.empty_cache()
