@@ -192,7 +192,8 @@ inline size_t stage_bytes(int64_t dim, int rows) {
   return (size_t)rows * (size_t)((dim + 511) / 512) * 128 * sizeof(float4);
 }
 
-// staged_rows: binary32 rows the staged layout keeps in LDS.
+// staged_rows: binary32 rows the staged layout keeps in LDS (0: the kernel
+// never stages; its waves load their modulation rows themselves).
 inline Shape row_shape(int64_t rows, int64_t per_mod, int64_t dim, int staged_rows) {
   Shape s;
   s.rows_per_wave = 1;
@@ -201,7 +202,8 @@ inline Shape row_shape(int64_t rows, int64_t per_mod, int64_t dim, int staged_ro
 #endif
   if (s.rows_per_wave < 1) s.rows_per_wave = 1;
   const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
-  s.staged = per_mod >= wg_rows && stage_bytes(dim, staged_rows) <= kMaxStagedLds;
+  s.staged = staged_rows > 0 && per_mod >= wg_rows &&
+             stage_bytes(dim, staged_rows) <= kMaxStagedLds;
 #ifdef DIT_TUNING
   if (getenv("DIT_NO_STAGING")) s.staged = false;
 #endif
