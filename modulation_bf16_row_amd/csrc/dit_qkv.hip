@@ -103,7 +103,7 @@ __device__ __forceinline__ void load_token(Token<HG> &t, const QkvArgs &a, int64
 }
 
 template <int HG, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_qk_norm_rope(
+__global__ __launch_bounds__(64 * kQkvWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_qk_norm_rope(
     QkvArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t total = a.batch * a.s_total;
@@ -168,7 +168,7 @@ static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {
   const dim3 grid((unsigned)((waves + kQkvWaves - 1) / kQkvWaves));
   switch (hg) {
 #define X(N) \
-  case N: DIT_LAUNCH((k_qk_norm_rope<N, MODE>), grid, dim3(256), 0, s, a); break;
+  case N: DIT_LAUNCH((k_qk_norm_rope<N, MODE>), grid, dim3(64 * kQkvWaves), 0, s, a); break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 #undef X
     default: return hipErrorInvalidValue;
