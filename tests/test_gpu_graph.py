@@ -1,9 +1,12 @@
 """Prepared calls and HIP-graph replays of the epilogues give the same bits as
 eager calls (and the oracle).
 
-The graph test replays a captured five-epilogue step several times, with
-eager work and synchronisations in between (the inputs are rewritten
-eagerly before each replay), and checks every replay against eager results.
+The graph test replays a captured step -- the five epilogues, the fused
+producers (with their E4M3 copies), the standalone modulate, the
+destination-major QKV epilogue and the Wan modulation table -- several
+times, with eager work and synchronisations in between (inputs and the
+E4M3 scale are rewritten in place before each replay, so a replay must read
+the new values), and checks every replay against eager results.
 """
 import numpy as np
 import pytest
@@ -61,6 +64,19 @@ class Step:
         S = q["cos"].shape[0]
         self.qkv_out = tuple(torch.empty((2, S, H, 128), dtype=torch.bfloat16, device="cuda")
                              for _ in range(3))
+        # fused producers, standalone modulate, destination-major QKV, modulation table
+        self.y = dev(synth.normal_bf16(tuple(self.x.shape), 1.0, seed + 11))
+        self.fs = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+        for k in ("rp", "gln", "ln8b", "grp8", "gln8", "mod"):
+            self.out[k] = torch.empty_like(self.x)
+        self.q8 = {k: torch.empty(tuple(self.x.shape), dtype=torch.uint8, device="cuda")
+                   for k in ("ln8", "gln8")}
+        self.packed = torch.empty((2, 2, S, 3, H // 2, 128), dtype=torch.bfloat16, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(seed + 13)
+        self.table = torch.randn((6, 256), device="cuda", generator=g) * 0.05
+        self.temb = (torch.randn((2, 40, 6, 256), device="cuda", generator=g) * 0.3).to(
+            torch.bfloat16)
+        self.mt = torch.empty((6, 2, 40, 256), dtype=torch.float32, device="cuda")
 
     def run(self, prepare=False):
         M = m()
@@ -74,16 +90,34 @@ class Step:
                                     prepare=prepare),
             M.dit_qk_norm_rope(self.txt, self.img, self.cos, self.sin, EPS, out=self.qkv_out,
                                prepare=prepare),
+            M.dit_gate_add_ln_modulate(self.res, self.y, self.g, self.sc, self.sh, EPS,
+                                       out_residual=self.out["rp"], out=self.out["gln"],
+                                       prepare=prepare),
+            M.dit_ln_modulate_fp8(self.x, self.sc, self.sh, self.fs, EPS, out=self.out["ln8b"],
+                                  out_fp8=self.q8["ln8"], prepare=prepare),
+            M.dit_gate_add_ln_modulate_fp8(self.res, self.y, self.g, self.sc, self.sh, self.fs,
+                                           EPS, out_residual=self.out["grp8"],
+                                           out=self.out["gln8"], out_fp8=self.q8["gln8"],
+                                           prepare=prepare),
+            M.dit_modulate_scale_shift(self.x, self.sc, self.sh, out=self.out["mod"],
+                                       prepare=prepare),
+            M.dit_qk_norm_rope_packed(self.txt, self.img, self.cos, self.sin, 2, EPS,
+                                      out=self.packed, prepare=prepare),
+            M.dit_wan_modulation_table(self.table, self.temb, out=self.mt, prepare=prepare),
         ]
         return calls
 
     def snapshot(self):
         torch.cuda.synchronize()
         return [host(self.out[k]) for k in ("ln", "rms", "tanh", "gate")] + \
-            [host(t) for t in self.qkv_out]
+            [host(t) for t in self.qkv_out] + \
+            [host(self.out[k]) for k in ("rp", "gln", "ln8b", "grp8", "gln8", "mod")] + \
+            [self.q8[k].cpu().numpy() for k in ("ln8", "gln8")] + \
+            [host(self.packed), self.mt.cpu().numpy().view(np.uint32)]
 
     def clear(self):
-        for t in list(self.out.values()) + list(self.qkv_out):
+        for t in list(self.out.values()) + list(self.qkv_out) + list(self.q8.values()) + \
+                [self.packed, self.mt]:
             t.zero_()
 
 
@@ -117,6 +151,8 @@ def test_graph_replays_match_eager():
         xn = synth.normal_bf16(tuple(s.x.shape), 1.0, 100 + rep)
         s.x.copy_(dev(xn))
         s.iq[0].copy_(dev(synth.normal_bf16(tuple(s.iq[0].shape), 1.0, 200 + rep)))
+        s.fs.fill_(0.05 * (rep + 1))                   # a new static E4M3 scale
+        s.temb.normal_(0.0, 0.3)
         torch.cuda.synchronize()
         s.clear()
         say(f"replay {rep}")
@@ -130,3 +166,5 @@ def test_graph_replays_match_eager():
         w = s.h
         assert_bits_equal(got[0], oracle.ln_modulate(xn, w["scale"], w["shift"], EPS),
                           f"replay {rep} ln vs oracle")
+        ref8 = oracle.ln_modulate_fp8(xn, w["scale"], w["shift"], EPS, 0.05 * (rep + 1))
+        assert np.array_equal(got[13], ref8[1]), f"replay {rep} E4M3 copy vs oracle"
