@@ -86,8 +86,6 @@ struct ModArgs {
   const uint16_t *x, *scale, *shift;
   int64_t out_rs, x_rs, mod_rs;
   int64_t rows, dim, per_mod;
-  int64_t rows_per_wave;       // set by the launcher
-  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct QkvStreamArgs {

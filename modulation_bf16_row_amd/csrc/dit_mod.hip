@@ -1,83 +1,82 @@
 // dit_mod.hip -- gfx950 standalone AdaLN modulate x * (1 + scale) + shift,
 // the elementwise step that follows a norm computed elsewhere (page
-// "基于Agent的SGLang扩散模型Kernel优化实践", section "实现拆解", the
-// modulate_scale_shift fast path), with the eager bf16 chain's three
-// roundings: bf(1 + scale), the product, the sum.
-// Geometry, staging and launch shapes: dit_rows.hpp; one_plus8: dit_ln.hpp.
+// "#34085 [diffusion] Clean up kernels and shared fast paths", section
+// "实现拆解", the modulate_scale_shift fast path), with the eager bf16
+// chain's three roundings: bf(1 + scale), the product, the sum.
+//
+// Geometry: nothing couples the elements of a row, so the rows are not held
+// by waves; the [rows, D] problem is covered as groups of 8 elements (one
+// 16-byte vector of x, of the scale row and of the shift row, one 16-byte
+// nontemporal store) in row-major order, one group per lane, by one-shot
+// 64-thread workgroups -- the layout that streams best on MI355X.  Per-batch
+// modulation rows are read with the default policy (they stay cached);
+// per-token ones, like x, stream.  Group g splits into row r = g / (D/8) and
+// modulation row r / (rows / mod_rows) by multiply-high division
+// (dit_divide.hpp) while g fits 32 bits; larger problems take a grid-stride
+// loop with 64-bit division.  one_plus8 and the row helpers: dit_ln.hpp,
+// dit_rows.hpp.
+#include "dit_divide.hpp"
 #include "dit_ln.hpp"
 
 namespace dit {
 
-// ---------------------------------------------------------------------------
-// out = bf(bf(x * bf(1 + scale)) + shift).
-// LDS (staged): [0] = bf(1 + scale), [1] = shift, binary32.
-// ---------------------------------------------------------------------------
-template <int NC, bool STAGED>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_modulate_scale_shift(
-    ModArgs a) {
-  extern __shared__ float4 lds[];
-  const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  constexpr int kRow = stage_vecs<NC>();
-  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
-                         : spans(a.rows, a.rows_per_wave);
-  if (STAGED) {
-    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
-      float s1[8], sh[8];
-      one_plus8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s1);
-      unpack8(load8(a.shift + sp.m * a.mod_rs + 8 * v), sh);
-      stage_put(lds, v, s1);
-      stage_put(lds + kRow, v, sh);
-    }
-    __syncthreads();
-  }
+constexpr int kModThreads = 64;
 
-  for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], sc[NC], sf[NC];
-    load_row<NC, kNtMod>(xv, a.x + r * a.x_rs, lane, dim);
-    if (!STAGED) {
-      const int64_t m = r / a.per_mod;
-      load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
-      load_mod_row<NC>(sf, a.shift + m * a.mod_rs, lane, dim, a.per_mod == 1);
-    }
-    uint16_t *orow = a.out + r * a.out_rs;
+// out = bf(bf(x * bf(1 + scale)) + shift) for the 8 elements of group i of
+// row r, modulation row m.
+__device__ __forceinline__ void modulate_group(const ModArgs &a, uint64_t r, uint64_t m,
+                                               uint64_t i) {
+  const V8 xv = kNtMod ? load8_stream(a.x + r * a.x_rs + 8 * i) : load8(a.x + r * a.x_rs + 8 * i);
+  const uint16_t *sp = a.scale + m * a.mod_rs + 8 * i, *hp = a.shift + m * a.mod_rs + 8 * i;
+  const bool per_token = a.per_mod == 1;
+  const V8 sc = per_token ? load8_stream(sp) : load8(sp);
+  const V8 sf = per_token ? load8_stream(hp) : load8(hp);
+  float s1[8], sh[8];
+  one_plus8(sc, s1);
+  unpack8(sf, sh);
+  V8 o;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!valid<NC>(c, lane, dim)) continue;
-      float s1[8], sh[8];
-      if (STAGED) {
-        stage_get(lds, c, lane, s1);
-        stage_get(lds + kRow, c, lane, sh);
-      } else {
-        one_plus8(sc[c], s1);
-        unpack8(sf[c], sh);
-      }
-      V8 o;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float p0 = lo(xv[c].w[k]) * s1[2 * k], p1 = hi(xv[c].w[k]) * s1[2 * k + 1];
-        round2(p0, p1);                                         // bf(x * (1 + scale))
-        o.w[k] = pack(p0 + sh[2 * k], p1 + sh[2 * k + 1]);      // + shift
-      }
-      store8(orow + 512 * c + 8 * lane, o);
-    }
+  for (int k = 0; k < 4; ++k) {
+    float p0 = lo(xv.w[k]) * s1[2 * k], p1 = hi(xv.w[k]) * s1[2 * k + 1];
+    round2(p0, p1);                                             // bf(x * (1 + scale))
+    o.w[k] = pack(p0 + sh[2 * k], p1 + sh[2 * k + 1]);          // + shift
   }
+  store8(a.out + r * a.out_rs + 8 * i, o);
 }
 
-static hipError_t mod_dispatch(ModArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 2);
-  a.rows_per_wave = sh.rows_per_wave;
-  a.blocks_per_mod = sh.blocks_per_mod;
-#define X(N)                                                                              \
-  case N:                                                                                 \
-    DIT_ROW_LAUNCH((k_modulate_scale_shift<N, true>), (k_modulate_scale_shift<N, false>), \
-                   stage_bytes(a.dim, 2), 0);                                             \
-    break;
-  DIT_ROW_DISPATCH();
-#undef X
+// 32-bit group indices: one group per lane.
+__global__ __launch_bounds__(kModThreads) void k_modulate_scale_shift(ModArgs a, uint32_t groups,
+                                                                      uint64_t m_row,
+                                                                      uint64_t m_mod) {
+  const uint32_t g = blockIdx.x * kModThreads + threadIdx.x;
+  if (g >= groups) return;
+  const uint32_t gpr = (uint32_t)(a.dim / 8);
+  const uint32_t r = div_by(g, m_row), i = g - r * gpr;
+  modulate_group(a, r, div_by(r, m_mod), i);
+}
+
+// 64-bit group indices, grid-stride.
+__global__ __launch_bounds__(kModThreads) void k_modulate_scale_shift_wide(ModArgs a) {
+  const uint64_t gpr = (uint64_t)a.dim / 8, groups = (uint64_t)a.rows * gpr;
+  const uint64_t step = (uint64_t)gridDim.x * kModThreads;
+  for (uint64_t g = (uint64_t)blockIdx.x * kModThreads + threadIdx.x; g < groups; g += step) {
+    const uint64_t r = g / gpr, i = g - r * gpr;
+    modulate_group(a, r, r / (uint64_t)a.per_mod, i);
+  }
 }
 
 hipError_t launch_modulate_scale_shift(const ModArgs &a, hipStream_t s) {
-  return mod_dispatch(a, s);
+  const uint64_t groups = (uint64_t)a.rows * (uint64_t)(a.dim / 8);
+  if (groups < (1ull << 32)) {
+    const dim3 grid((unsigned)((groups + kModThreads - 1) / kModThreads));
+    DIT_LAUNCH(k_modulate_scale_shift, grid, dim3(kModThreads), 0, s, a, (uint32_t)groups,
+               reciprocal((uint64_t)(a.dim / 8)), reciprocal((uint64_t)a.per_mod));
+  } else {
+    const uint64_t blocks = (groups + kModThreads - 1) / kModThreads;
+    const dim3 grid((unsigned)(blocks < 0x7FFFFFFF ? blocks : 0x7FFFFFFF));
+    DIT_LAUNCH(k_modulate_scale_shift_wide, grid, dim3(kModThreads), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dit

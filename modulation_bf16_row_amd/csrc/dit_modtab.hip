@@ -18,24 +18,16 @@
 // lane.
 //
 // Index arithmetic: a lane's group g splits into output row r = g / (D/4)
-// and row r into chunk k = r / (B*S) and token t.  While every group index
-// fits 32 bits, both quotients are exact multiply-high products with a
-// reciprocal computed on the host (Granlund and Montgomery, "Division by
-// invariant integers using multiplication", PLDI 1994): for 2 <= d < 2^32
-// and M = floor(2^64 / d) + 1, the error term n * (M d - 2^64) < 2^64 for
-// every n < 2^32, so floor(n M / 2^64) = floor(n / d).  Larger problems
+// and row r into chunk k = r / (B*S) and token t, by multiply-high division
+// (dit_divide.hpp) while every group index fits 32 bits; larger problems
 // take a grid-stride loop with 64-bit division.
 #include "dit_device.hpp"
+#include "dit_divide.hpp"
 #include "dit_launch.hpp"
 
 namespace dit {
 
 constexpr int kModtabThreads = 64;
-
-// floor(n / d) from M = floor(2^64 / d) + 1; M == 0 stands for d == 1.
-__device__ __forceinline__ uint32_t div_by(uint32_t n, uint64_t m) {
-  return m ? (uint32_t)__umul64hi((uint64_t)n, m) : n;
-}
 
 // Output group gi (4 floats) of row (k, t): table[k] + temb[t][k].
 __device__ __forceinline__ void table_group(const ModTableArgs &a, uint64_t k, uint64_t t,
@@ -69,13 +61,6 @@ __global__ __launch_bounds__(kModtabThreads) void k_wan_mod_table_wide(ModTableA
     const uint64_t k = r / tokens, t = r - k * tokens;
     table_group(a, k, t, gi, g);
   }
-}
-
-// floor(2^64 / d) + 1 for 2 <= d < 2^32, 0 for d == 1.
-static uint64_t reciprocal(uint64_t d) {
-  if (d < 2) return 0;
-  const uint64_t q = ~0ull / d, rem = ~0ull % d;     // 2^64 - 1 = q d + rem
-  return q + (rem == d - 1 ? 1 : 0) + 1;             // d | 2^64 exactly when rem == d - 1
 }
 
 hipError_t launch_wan_mod_table(const ModTableArgs &a, hipStream_t s) {
