@@ -1,59 +1,76 @@
-// dit_gate.hip -- gfx950 residual gate-add.
-// Geometry, staging and launch shapes: dit_rows.hpp.
+// dit_gate.hip -- gfx950 residual gate-add, out = bf(residual + bf(gate * y))
+// (page "AI Agent 驱动的 SGLang Kernel 一等公民", section 0x3 / 3.2,
+// residual+gate*update; page "#34085 [diffusion] Clean up kernels and shared
+// fast paths", section "实现拆解", residual_gate_add).
+//
+// Geometry: nothing couples the elements of a row, so the rows are not held
+// by waves; the [rows, D] problem is covered as groups of 8 elements (one
+// 16-byte vector each of residual, y and the gate row, one 16-byte
+// nontemporal store) in row-major order, one group per lane, by one-shot
+// 64-thread workgroups -- the layout that streams best on MI355X.  Per-batch
+// gate rows are read with the default policy (they stay cached); per-token
+// ones stream with residual and y.  Group g splits into row r = g / (D/8)
+// and gate row r / (rows / mod_rows) by multiply-high division
+// (dit_divide.hpp) while g fits 32 bits; larger problems take a grid-stride
+// loop with 64-bit division.  Row helpers: dit_rows.hpp.
+#include "dit_divide.hpp"
 #include "dit_rows.hpp"
 
 namespace dit {
 
-// ---------------------------------------------------------------------------
-// Residual gate-add: out = bf(residual + bf(gate * y)).
-// Never staged: with two row streams and two roundings per element the
-// kernel has too little arithmetic to hide a workgroup's LDS conversion and
-// barrier; its waves read the gate row themselves (an L2 hit for per-batch
-// gates).  At the Qwen-Image shape this measured 29.0 us against 29.9 us
-// with the gate staged in LDS.
-// ---------------------------------------------------------------------------
-template <int NC>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_residual_gate_add(
-    GateAddArgs a) {
-  const int lane = threadIdx.x & 63, dim = (int)a.dim;
-  const Span sp = spans(a.rows, a.rows_per_wave);
-  for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 rv[NC], yv[NC], gv[NC];
-    load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
-    load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
-    load_mod_row<NC>(gv, a.gate + (r / a.per_mod) * a.mod_rs, lane, dim, a.per_mod == 1);
-    uint16_t *orow = a.out + r * a.out_rs;
+constexpr int kGateThreads = 64;
+
+// Group i of row r with gate row m.
+__device__ __forceinline__ void gate_group(const GateAddArgs &a, uint64_t r, uint64_t m,
+                                           uint64_t i) {
+  const uint16_t *rp = a.residual + r * a.res_rs + 8 * i, *yp = a.y + r * a.y_rs + 8 * i;
+  const V8 rv = kNtGate ? load8_stream(rp) : load8(rp);
+  const V8 yv = kNtGate ? load8_stream(yp) : load8(yp);
+  const uint16_t *gp = a.gate + m * a.mod_rs + 8 * i;
+  const V8 gv = a.per_mod == 1 ? load8_stream(gp) : load8(gp);
+  V8 o;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!valid<NC>(c, lane, dim)) continue;
-      float g[8];
-      unpack8(gv[c], g);
-      V8 o;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float q0 = g[2 * k] * lo(yv[c].w[k]), q1 = g[2 * k + 1] * hi(yv[c].w[k]);
-        round2(q0, q1);                                         // bf(gate * y)
-        o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
-      }
-      store8(orow + 512 * c + 8 * lane, o);
-    }
+  for (int k = 0; k < 4; ++k) {
+    float q0 = lo(gv.w[k]) * lo(yv.w[k]), q1 = hi(gv.w[k]) * hi(yv.w[k]);
+    round2(q0, q1);                                             // bf(gate * y)
+    o.w[k] = pack(lo(rv.w[k]) + q0, hi(rv.w[k]) + q1);
+  }
+  store8(a.out + r * a.out_rs + 8 * i, o);
+}
+
+// 32-bit group indices: one group per lane.
+__global__ __launch_bounds__(kGateThreads) void k_residual_gate_add(GateAddArgs a, uint32_t groups,
+                                                                    uint64_t m_row,
+                                                                    uint64_t m_mod) {
+  const uint32_t g = blockIdx.x * kGateThreads + threadIdx.x;
+  if (g >= groups) return;
+  const uint32_t gpr = (uint32_t)(a.dim / 8);
+  const uint32_t r = div_by(g, m_row), i = g - r * gpr;
+  gate_group(a, r, div_by(r, m_mod), i);
+}
+
+// 64-bit group indices, grid-stride.
+__global__ __launch_bounds__(kGateThreads) void k_residual_gate_add_wide(GateAddArgs a) {
+  const uint64_t gpr = (uint64_t)a.dim / 8, groups = (uint64_t)a.rows * gpr;
+  const uint64_t step = (uint64_t)gridDim.x * kGateThreads;
+  for (uint64_t g = (uint64_t)blockIdx.x * kGateThreads + threadIdx.x; g < groups; g += step) {
+    const uint64_t r = g / gpr, i = g - r * gpr;
+    gate_group(a, r, r / (uint64_t)a.per_mod, i);
   }
 }
 
-static hipError_t gate_add_dispatch(GateAddArgs a, hipStream_t s) {
-  const Shape sh = row_shape(a.rows, a.per_mod, a.dim, 0);
-  a.rows_per_wave = sh.rows_per_wave;
-  a.blocks_per_mod = sh.blocks_per_mod;
-#define X(N)                                                                              \
-  case N:                                                                                 \
-    DIT_LAUNCH((k_residual_gate_add<N>), sh.grid, dim3(kThreads), 0, s, a);               \
-    break;
-  DIT_ROW_DISPATCH();
-#undef X
-}
-
 hipError_t launch_residual_gate_add(const GateAddArgs &a, hipStream_t s) {
-  return gate_add_dispatch(a, s);
+  const uint64_t groups = (uint64_t)a.rows * (uint64_t)(a.dim / 8);
+  if (groups < (1ull << 32)) {
+    const dim3 grid((unsigned)((groups + kGateThreads - 1) / kGateThreads));
+    DIT_LAUNCH(k_residual_gate_add, grid, dim3(kGateThreads), 0, s, a, (uint32_t)groups,
+               reciprocal((uint64_t)(a.dim / 8)), reciprocal((uint64_t)a.per_mod));
+  } else {
+    const uint64_t blocks = (groups + kGateThreads - 1) / kGateThreads;
+    const dim3 grid((unsigned)(blocks < 0x7FFFFFFF ? blocks : 0x7FFFFFFF));
+    DIT_LAUNCH(k_residual_gate_add_wide, grid, dim3(kGateThreads), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dit

@@ -77,8 +77,6 @@ struct GateAddArgs {
   const uint16_t *residual, *y, *gate;
   int64_t out_rs, res_rs, y_rs, mod_rs;
   int64_t rows, dim, per_mod;
-  int64_t rows_per_wave;       // set by the launcher
-  int64_t blocks_per_mod;      // set by the launcher (staged layout)
 };
 
 struct ModArgs {
