@@ -3,7 +3,8 @@
   python -m modulation_bf16_row_amd.profiling trace RESULTS.db OUT.txt --command "..."
       per-kernel dispatch statistics from a --kernel-trace run
   python -m modulation_bf16_row_amd.profiling traffic FETCH.db WRITE.db OUT.txt \
-        --kernel k_ln_modulate --calib k_probe_copy --calib-bytes 1073741824 --command "..."
+        --kernel k_ln_modulate [--grid N] --calib k_probe_copy --calib-bytes 1073741824 \
+        --command "..."
       HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE runs,
       each scaled by what the same counter reads for a copy dispatch of known
       size (calib-bytes read and calib-bytes written)
@@ -40,58 +41,59 @@ def _short(name):
 
 
 def kernel_stats(db):
+    """Per (kernel, grid size in work-items) dispatch statistics, largest total first."""
     con = sqlite3.connect(db)
-    rows = con.execute("select name, duration from kernels").fetchall()
+    rows = con.execute("select name, duration, grid_x * grid_y * grid_z from kernels").fetchall()
     by = {}
-    for name, dur in rows:
-        by.setdefault(_short(name), []).append(dur / 1000.0)
+    for name, dur, grid in rows:
+        by.setdefault((_short(name), int(grid)), []).append(dur / 1000.0)
     out = []
-    for name, d in by.items():
+    for (name, grid), d in by.items():
         d = sorted(d)
         pct = lambda q: d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))]
-        out.append((name, len(d), statistics.mean(d), statistics.median(d), pct(0.1), pct(0.9),
-                    d[0], d[-1], sum(d)))
+        out.append((name, grid, len(d), statistics.mean(d), statistics.median(d), pct(0.1),
+                    pct(0.9), d[0], d[-1], sum(d)))
     return sorted(out, key=lambda r: -r[-1])
 
 
 def counter_values(db, counter):
-    """kernel name -> list of per-dispatch values of one counter."""
+    """(kernel name, grid size) -> list of per-dispatch values of one counter."""
     con = sqlite3.connect(db)
-    rows = con.execute("select kernel_name, value from counters_collection where "
+    rows = con.execute("select kernel_name, grid_size, value from counters_collection where "
                        "counter_name = ?", (counter,)).fetchall()
     by = {}
-    for name, v in rows:
-        by.setdefault(_short(name), []).append(float(v))
+    for name, grid, v in rows:
+        by.setdefault((_short(name), int(grid)), []).append(float(v))
     return by
 
 
-def _match(by, pattern):
-    keys = [k for k in by if re.search(pattern, k)]
+def _match(by, pattern, grid=None):
+    keys = [k for k in by if re.search(pattern, k[0]) and (grid is None or k[1] == grid)]
     if not keys:
-        raise SystemExit(f"no dispatch of {pattern!r} in {sorted(by)}")
+        raise SystemExit(f"no dispatch of {pattern!r} (grid {grid}) in {sorted(by)}")
     vals = [v for k in keys for v in by[k]]
     return statistics.mean(vals), len(vals)
 
 
 def write_trace(db, out, command):
-    lines = [f"# rocprofv3 kernel-trace summary (durations in microseconds)",
+    lines = [f"# rocprofv3 kernel-trace summary (durations in microseconds; grid in work-items)",
              f"# command: {command}",
              f"# kernel_source_hash = {kernel_source_hash()}",
-             f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'p10_us':>9s} "
-             f"{'p90_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>11s}"]
-    for name, n, avg, med, p10, p90, lo, hi, tot in kernel_stats(db):
-        lines.append(f"{name[:40]:40s} {n:6d} {avg:9.3f} {med:9.3f} {p10:9.3f} {p90:9.3f} "
-                     f"{lo:9.3f} {hi:9.3f} {tot:11.1f}")
+             f"{'kernel':40s} {'grid':>10s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} "
+             f"{'p10_us':>9s} {'p90_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>11s}"]
+    for name, grid, n, avg, med, p10, p90, lo, hi, tot in kernel_stats(db):
+        lines.append(f"{name[:40]:40s} {grid:10d} {n:6d} {avg:9.3f} {med:9.3f} {p10:9.3f} "
+                     f"{p90:9.3f} {lo:9.3f} {hi:9.3f} {tot:11.1f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command):
+def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, grid=None):
     fetch = counter_values(fetch_db, "FETCH_SIZE")
     write = counter_values(write_db, "WRITE_SIZE")
-    f_k, nf = _match(fetch, kernel)
-    w_k, nw = _match(write, kernel)
+    f_k, nf = _match(fetch, kernel, grid)
+    w_k, nw = _match(write, kernel, grid)
     f_c, _ = _match(fetch, calib)
     w_c, _ = _match(write, calib)
     f_scale = calib_bytes / (f_c * 1024.0)
@@ -104,6 +106,7 @@ def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command):
         f"# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by "
         f"calib_bytes / (counter of the copy dispatch)",
         f"kernel = {kernel}",
+        f"grid_work_items = {grid if grid is not None else 'any'}",
         f"dispatches_fetch = {nf}",
         f"dispatches_write = {nw}",
         f"fetch_kib_per_dispatch = {f_k:.1f}",
@@ -138,12 +141,15 @@ def main():
     c.add_argument("--kernel", required=True)
     c.add_argument("--calib", default="k_probe_copy")
     c.add_argument("--calib-bytes", type=float, default=float(1 << 30))
+    c.add_argument("--grid", type=int, default=None,
+                   help="only dispatches of this grid size (work-items)")
     c.add_argument("--command", default="")
     a = ap.parse_args()
     if a.cmd == "trace":
         write_trace(a.db, a.out, a.command)
     else:
-        write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command)
+        write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command,
+                      a.grid)
 
 
 if __name__ == "__main__":
