@@ -1,6 +1,8 @@
-// dit_rows.hpp -- shared pieces of the gfx950 row kernels (dit_ln.hip,
-// dit_rms.hip, dit_gate.hip): geometry, row and modulation loads, binary32
-// LDS staging, row runs and launch shapes.
+// dit_rows.hpp -- shared pieces of the gfx950 row kernels, whose rows carry a
+// reduction (dit_ln.hip, dit_gate_ln.hip, dit_rms.hip): geometry, row and
+// modulation loads, binary32 LDS staging, row runs and launch shapes.  The
+// elementwise kernels (dit_gate.hip, dit_mod.hip) use the vector helpers and
+// load policies only.
 //
 // Geometry.  One 64-lane wave per row at a time; lane l owns the 8-element
 // vectors at 512c + 8l of chunk c (c < NC = ceil(dim / 512)), each moved
@@ -16,7 +18,7 @@
 // modulation row, so all rows of a workgroup share it.  The workgroup
 // converts its per-element operands once into LDS as binary32 values --
 // bf(1 + scale) and shift, the RMSNorm weight and scale, tanh(gate), or
-// gate -- and the waves read them with two 128-bit LDS accesses per
+// gate, bf(1 + scale) and shift -- and the waves read them with two 128-bit LDS accesses per
 // 8-element vector, with no bf16 unpacking in the row loop (the kernels
 // are close to their vector-ALU budget, so every instruction per element
 // counts).  With per-token modulation rows are laid out consecutively and
@@ -30,8 +32,8 @@
 // LayerNorm/AdaLN producer -- same page, sections "将FP8量化融合到前序算子" and
 // "NVFP4的三组优化"; native bf16 RMSNorm chain -- page "#34085 [diffusion] Clean
 // up kernels and shared fast paths", section "关键源码片段";
-// rmsnorm+tanh(gate)*x+residual and residual+gate*update -- page "AI Agent
-// 驱动的 SGLang Kernel 一等公民", section 0x3 / 3.2.
+// rmsnorm+tanh(gate)*x+residual -- page "AI Agent 驱动的 SGLang Kernel
+// 一等公民", section 0x3 / 3.2.
 #pragma once
 
 #include <stdlib.h>

@@ -22,13 +22,38 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+def _code_only(text):
+    """Source text without comments and whitespace (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources and headers the kernels are built from."""
+    """Hash of the code (comments and whitespace excluded) of the HIP sources
+    and headers the kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
