@@ -98,7 +98,9 @@ def read_traffic(kernel):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
     from modulation_bf16_row_amd.profiling import kernel_source_hash
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    source = vals.get("kernel_source")
+    source = None if source in (None, "all of csrc") else source
+    if vals.get("kernel_source_hash") != kernel_source_hash(source):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

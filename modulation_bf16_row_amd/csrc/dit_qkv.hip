@@ -149,6 +149,8 @@ __global__ __launch_bounds__(64 * kQkvWaves) __attribute__((amdgpu_waves_per_eu(
 // ceil(heads / 4) groups split into as few equal parts as that allows.  At
 // the Qwen-Image shape (24 heads) one group per wave (70 VGPRs, 7 waves per
 // SIMD) measured 57.3 us against 58.4, 59.8 and 64.4 us for 2, 3 and 6.
+// Only HG = 1 is built into the library; the tuning build instantiates up to
+// 16 groups per wave for such sweeps.
 constexpr int64_t kQkvTargetWaves = int64_t(1) << 20;
 constexpr int kQkvGroups = 1;
 
@@ -169,7 +171,10 @@ static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {
   switch (hg) {
 #define X(N) \
   case N: DIT_LAUNCH((k_qk_norm_rope<N, MODE>), grid, dim3(64 * kQkvWaves), 0, s, a); break;
-    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+    X(1)
+#ifdef DIT_TUNING
+    X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+#endif
 #undef X
     default: return hipErrorInvalidValue;
   }

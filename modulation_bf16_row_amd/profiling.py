@@ -9,7 +9,8 @@
       each scaled by what the same counter reads for a copy dispatch of known
       size (calib-bytes read and calib-bytes written)
 
-The traffic summary records a hash of the kernel sources; the benchmark only
+The traffic summary records a hash of the code of the kernel's translation
+unit (--source) or of all kernel sources; the benchmark only
 reports it while the sources still match.
 """
 import argparse
@@ -46,13 +47,31 @@ def _code_only(text):
     return "".join(out)
 
 
-def kernel_source_hash():
-    """Hash of the code (comments and whitespace excluded) of the HIP sources
-    and headers the kernels are built from."""
+CSRC = os.path.join(PKG, "csrc")
+
+
+def unit_files(source):
+    """The file `source` of csrc/ and every csrc/ header it includes,
+    directly or through other headers (#include "...")."""
+    seen, todo = set(), [source]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(CSRC, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), flags=re.M)
+    return sorted(seen)
+
+
+def kernel_source_hash(source=None):
+    """Hash of the code (comments and whitespace excluded) of the kernel
+    sources: of one translation unit (`source`, e.g. "dit_ln.hip", and the
+    headers it includes) or, with no argument, of every file in csrc/."""
+    names = unit_files(source) if source else sorted(os.listdir(CSRC))
     h = hashlib.sha256()
-    csrc = os.path.join(PKG, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+    for name in names:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
@@ -114,7 +133,8 @@ def write_trace(db, out, command):
     print("\n".join(lines))
 
 
-def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, grid=None):
+def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, grid=None,
+                  source=None):
     fetch = counter_values(fetch_db, "FETCH_SIZE")
     write = counter_values(write_db, "WRITE_SIZE")
     f_k, nf = _match(fetch, kernel, grid)
@@ -145,7 +165,8 @@ def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, 
         f"hbm_read_bytes_per_launch = {read_b:.0f}",
         f"hbm_write_bytes_per_launch = {write_b:.0f}",
         f"hbm_bytes_per_launch = {read_b + write_b:.0f}",
-        f"kernel_source_hash = {kernel_source_hash()}",
+        f"kernel_source = {source or 'all of csrc'}",
+        f"kernel_source_hash = {kernel_source_hash(source)}",
     ]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -168,13 +189,15 @@ def main():
     c.add_argument("--calib-bytes", type=float, default=float(1 << 30))
     c.add_argument("--grid", type=int, default=None,
                    help="only dispatches of this grid size (work-items)")
+    c.add_argument("--source", default=None,
+                   help="csrc file defining the kernel; its translation unit is hashed")
     c.add_argument("--command", default="")
     a = ap.parse_args()
     if a.cmd == "trace":
         write_trace(a.db, a.out, a.command)
     else:
         write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command,
-                      a.grid)
+                      a.grid, a.source)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,53 @@
+"""CPU tests of the profile-summary helpers: the kernel-source hash that ties a
+counter summary to the code it was taken on follows code, not comments, and
+covers exactly the headers a translation unit includes."""
+import os
+import shutil
+
+import pytest
+
+from modulation_bf16_row_amd import profiling
+
+
+def test_code_only_strips_comments_and_whitespace_keeps_literals():
+    src = 'int a = 1; // note\n/* block\n comment */ const char *s = "x // y"; char q = \'"\';\n'
+    assert profiling._code_only(src) == 'inta=1;constchar*s="x // y";charq=\'"\';'
+
+
+def test_unit_files_follow_local_includes():
+    files = profiling.unit_files("dit_ln.hip")
+    assert {"dit_ln.hip", "dit_ln.hpp", "dit_rows.hpp", "dit_device.hpp",
+            "dit_launch.hpp"} <= set(files)
+    assert "dit_qkv.hip" not in files
+    assert "dit_divide.hpp" in profiling.unit_files("dit_modtab.hip")
+
+
+@pytest.fixture
+def csrc_copy(tmp_path, monkeypatch):
+    d = tmp_path / "csrc"
+    shutil.copytree(profiling.CSRC, d)
+    monkeypatch.setattr(profiling, "CSRC", str(d))
+    return d
+
+
+def _edit(path, old, new):
+    text = path.read_text(encoding="utf-8")
+    assert old in text
+    path.write_text(text.replace(old, new, 1), encoding="utf-8")
+
+
+def test_hash_ignores_comment_edits_and_sees_code_edits(csrc_copy):
+    h_unit, h_all = profiling.kernel_source_hash("dit_ln.hip"), profiling.kernel_source_hash()
+    _edit(csrc_copy / "dit_ln.hip", "// dit_ln.hip", "//   dit_ln.hip (edited comment)")
+    assert profiling.kernel_source_hash("dit_ln.hip") == h_unit
+    assert profiling.kernel_source_hash() == h_all
+    _edit(csrc_copy / "dit_ln.hip", "namespace dit {", "namespace dit {\nconstexpr int kUnused = 1;")
+    assert profiling.kernel_source_hash("dit_ln.hip") != h_unit
+
+
+def test_unit_hash_sees_included_headers_only(csrc_copy):
+    h_ln = profiling.kernel_source_hash("dit_ln.hip")
+    h_qkv = profiling.kernel_source_hash("dit_qkv.hip")
+    _edit(csrc_copy / "dit_rows.hpp", "namespace dit {", "namespace dit {\nconstexpr int kX = 2;")
+    assert profiling.kernel_source_hash("dit_ln.hip") != h_ln      # dit_ln.hip includes it
+    assert profiling.kernel_source_hash("dit_qkv.hip") == h_qkv    # dit_qkv.hip does not
