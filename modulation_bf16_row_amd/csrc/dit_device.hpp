@@ -308,14 +308,37 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false) & 0xFFFFu;
 }
 
-// E4M3 codes of the eight bf16 values of v divided by s (IEEE division), as
-// two words (codes of elements 0-3, 4-7).
-__device__ __forceinline__ void quant8(const uint32_t (&w)[4], float s, uint32_t &q0,
+// The binary32 quotient v / s of a bf16 value v by a binary32 scale s, for the
+// E4M3 copy, as one binary64 product with r = 1 / (double)s (computed once
+// per wave with the correctly rounded binary64 division):
+// (float)((double)v * r).  Wherever the IEEE binary32 quotient is a normal
+// number the two are equal bit for bit: v = X 2^b with X < 2^8, s = S 2^a
+// with S < 2^24, and a midpoint between normal binary32 numbers has an odd
+// significand M >= 2^24 + 1, so X 2^d = M S has no solution -- v / s is never
+// a midpoint -- and |v / s - m| >= |m| 2^-49 for every midpoint m; the
+// binary64 product is within 2^-51.9 |v / s| of v / s (two roundings at
+// 2^-53, no underflow or overflow for any binary32 operands), so it rounds
+// to the same binary32 value.  Where the quotient is subnormal (below
+// 2^-126) the two may differ in the last places, but every such value -- and
+// the exact one -- has the E4M3 code +0 or -0 of its sign.  Zero, infinite
+// and NaN operands give the IEEE results (x * 0 for s = inf, x * inf for
+// s = 0, NaN for 0 / 0 and inf / inf).
+__device__ __forceinline__ float div_by_scale(float v, double r) {
+  return (float)((double)v * r);
+}
+
+// E4M3 codes of the eight bf16 values of v divided by the scale (r = 1 /
+// (double)s, see div_by_scale), as two words (codes of elements 0-3, 4-7).
+__device__ __forceinline__ void quant8(const uint32_t (&w)[4], double r, uint32_t &q0,
                                        uint32_t &q1) {
-  q0 = e4m3x2(__uint_as_float(w[0] << 16) / s, __uint_as_float(w[0] & 0xFFFF0000u) / s) |
-       (e4m3x2(__uint_as_float(w[1] << 16) / s, __uint_as_float(w[1] & 0xFFFF0000u) / s) << 16);
-  q1 = e4m3x2(__uint_as_float(w[2] << 16) / s, __uint_as_float(w[2] & 0xFFFF0000u) / s) |
-       (e4m3x2(__uint_as_float(w[3] << 16) / s, __uint_as_float(w[3] & 0xFFFF0000u) / s) << 16);
+  q0 = e4m3x2(div_by_scale(__uint_as_float(w[0] << 16), r),
+              div_by_scale(__uint_as_float(w[0] & 0xFFFF0000u), r)) |
+       (e4m3x2(div_by_scale(__uint_as_float(w[1] << 16), r),
+               div_by_scale(__uint_as_float(w[1] & 0xFFFF0000u), r)) << 16);
+  q1 = e4m3x2(div_by_scale(__uint_as_float(w[2] << 16), r),
+              div_by_scale(__uint_as_float(w[2] & 0xFFFF0000u), r)) |
+       (e4m3x2(div_by_scale(__uint_as_float(w[3] << 16), r),
+               div_by_scale(__uint_as_float(w[3] & 0xFFFF0000u), r)) << 16);
 }
 
 __device__ __forceinline__ float elem(const V8 &v, int j) {

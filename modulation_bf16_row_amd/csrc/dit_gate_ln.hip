@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_m
   constexpr int kRow = stage_vecs<NC>();
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
-  const float qs = F8 ? *a.fp8_scale : 1.0f;
+  const double qr = F8 ? 1.0 / (double)*a.fp8_scale : 1.0;   // E4M3 copy: 1 / scale
   if (STAGED) {
     for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
       const int64_t off = sp.m * a.mod_rs + 8 * v;
@@ -75,13 +75,13 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_m
     uint8_t *qrow = F8 ? a.out8 + r * a.out8_rs : nullptr;
     if (STAGED) {
       phase_barrier();
-      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+      ln_modulate_out<NC, F8>(orow, qrow, qr, d, rho, lane, dim,
                               [&](int c, float (&s1)[8], float (&sh)[8]) {
                                 stage_get(lds + kRow, c, lane, s1);
                                 stage_get(lds + 2 * kRow, c, lane, sh);
                               });
     } else {
-      ln_modulate_out<NC, F8>(orow, qrow, qs, d, rho, lane, dim,
+      ln_modulate_out<NC, F8>(orow, qrow, qr, d, rho, lane, dim,
                               [&](int c, float (&s1)[8], float (&sh)[8]) {
                                 one_plus8(sc[c], s1);
                                 unpack8(sf[c], sh);

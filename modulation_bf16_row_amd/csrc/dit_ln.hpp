@@ -51,9 +51,10 @@ __device__ __forceinline__ void one_plus8(const V8 &s, float (&f)[8]) {
 }
 
 // out = bf(bf(bf(d * rho) * s1) + shift); mod(c, s1, sh) gives chunk c's
-// bf(1 + scale) and shift as binary32 values.  F8: also qrow = E4M3(out / qs).
+// bf(1 + scale) and shift as binary32 values.  F8: also qrow = E4M3(out / s),
+// qr = 1 / (double)s (dit_device.hpp, div_by_scale).
 template <int NC, bool F8, class Mod>
-__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, uint8_t *qrow, float qs,
+__device__ __forceinline__ void ln_modulate_out(uint16_t *orow, uint8_t *qrow, double qr,
                                                 const float (&d)[NC][8], float rho, int lane,
                                                 int dim, Mod mod) {
 #pragma unroll
@@ -73,7 +74,7 @@ __device__ __forceinline__ void ln_modulate_out(uint16_t *orow, uint8_t *qrow, f
     store8(orow + 512 * c + 8 * lane, o);
     if (F8) {
       uint32_t q0, q1;
-      quant8(o.w, qs, q0, q1);
+      quant8(o.w, qr, q0, q1);
       store8b(qrow + 512 * c + 8 * lane, q0, q1);
     }
   }

@@ -132,7 +132,8 @@ __global__ void k_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, con
   if (op == 0) {
     v = static_cast<const float *>(in)[i];
   } else {
-    v = __uint_as_float((uint32_t) static_cast<const uint16_t *>(in)[i] << 16) / *scale;
+    v = div_by_scale(__uint_as_float((uint32_t) static_cast<const uint16_t *>(in)[i] << 16),
+                     1.0 / (double)*scale);
   }
   out[i] = (uint8_t)(e4m3x2(v, 0.0f) & 0xFFu);
 }

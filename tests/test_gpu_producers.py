@@ -157,7 +157,8 @@ def test_e4m3_conversion_every_input_in_range():
     _e4m3_equal(got, oracle.e4m3(bits.view(np.float32)), "negatives and edges")
 
 
-@pytest.mark.parametrize("fp8_scale", [1.0, 3.1, 0.3, 0.0173, 2.0 ** -3, 179.2])
+@pytest.mark.parametrize("fp8_scale", [1.0, 3.1, 0.3, 0.0173, 2.0 ** -3, 179.2, -0.37,
+                                       2.0 ** -140, 3.0e38, 1e-30, 0.0])
 def test_fp8_quantization_every_bf16(fp8_scale):
     """E4M3(h / s) for every bf16 h: the kernels' division and conversion
     against an IEEE binary32 division and the oracle's encoder."""
