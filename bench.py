@@ -24,6 +24,9 @@ names; per-kernel durations (mean, median, p10, p90) come from further steps
 launched eagerly from prepared calls, each dispatch recording its own
 start/stop events, in blocks that interleave the two modes (main, other,
 other, main); the other mode's figures are reported beside them.
+Each step kernel is also timed on its own, back to back over four buffer
+sets (kernels_alone), as context: an in-step duration also carries part of
+the preceding kernel's write drain.
 Beside the step, the fused producers (gated residual + LN, the E4M3 dual
 outputs), the standalone modulate, the destination-major QKV epilogue and the
 Wan 720p block's kernels (75600 x 5120, per-token modulation, the modulation
@@ -178,6 +181,36 @@ def make_plans(m, s, mode):
         "qk_norm_rope": m.dit_qk_norm_rope(s.txt, s.img, s.cos, s.sin, EPS, mode,
                                            out=s.qkv_out, prepare=True),
     }
+
+
+def time_alone(m, torch, sets, mode, reps=40):
+    """Each step kernel on its own: `reps` back-to-back launches rotating over
+    the buffer sets (four: a set's operands were last touched three launches
+    earlier, beyond what the 256 MB Infinity Cache holds), each dispatch timed
+    by its own events.  Context for the in-step durations, which also carry
+    part of the preceding kernel's write drain."""
+    plans = [make_plans(m, s, mode) for s in sets]
+    res = {}
+    for k in KERNELS:
+        for p in plans:
+            p[k]()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            m.dit_time_next_launch(*ev[i])
+            plans[i % len(plans)][k]()
+        torch.cuda.synchronize()
+        us_list = [1000.0 * a.elapsed_time(b) for a, b in ev]
+        us = float(np.mean(us_list))
+        gbs = BYTES[k] / (us * 1e-6) / 1e9
+        res[k] = dict(us=round(us, 2), median_us=round(float(np.median(us_list)), 2),
+                      gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4))
+    res["note"] = ("each kernel back to back over %d buffer sets; the roofline uses the "
+                   "in-step durations" % len(sets))
+    return res
 
 
 def time_producers(m, torch, sets, mode, steps):
@@ -606,6 +639,7 @@ def main():
 
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    extra = [BufferSet(blk, qkv, torch), BufferSet(blk, qkv, torch)]   # for time_alone
     dom = "ln_modulate"
     achieved = per_kernel[dom]["gbs"]
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
@@ -626,6 +660,7 @@ def main():
         **{"kernels_" + other: per_kernel_other},
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
+        kernels_alone=time_alone(m, torch, sets + extra, args.mode),
         producers=time_producers(m, torch, sets, args.mode, args.steps),
         wan720p=time_wan(m, torch, args.mode),
         copy_ceiling_gbs=copy_ceiling(m, torch),
