@@ -233,7 +233,8 @@ def _qkv_ref(txt, img, wts, cos_t, sin_t, H):
 
 
 @pytest.mark.parametrize("B,S_txt,S_img,H", [(2, 3, 5, 24), (1, 0, 7, 24), (2, 5, 0, 4),
-                                             (3, 2, 9, 5), (1, 1, 1, 1), (2, 64, 256, 24)])
+                                             (3, 2, 9, 5), (1, 1, 1, 1), (2, 64, 256, 24),
+                                             (1, 2, 3, 64), (2, 3, 2, 63)])
 @pytest.mark.parametrize("joint", [False, True])
 def test_qk_norm_rope(B, S_txt, S_img, H, joint):
     got, inp = _run_qkv(B, S_txt, S_img, H, 40 + H + S_img, joint=joint)
