@@ -12,8 +12,11 @@ namespace dit {
 // F8: also the E4M3 copy out8 = E4M3(out / s).
 // LDS (staged): [0] = gate, [1] = bf(1 + scale), [2] = shift, binary32.
 // ---------------------------------------------------------------------------
+// Register budget: the per-token form holds five row-sized operands (residual,
+// y, gate, scale and shift rows), so it asks for one wave per SIMD fewer than
+// the staged form; with the staged form's budget it spilled at NC = 7, 11, 12.
 template <int NC, int MODE, bool STAGED, bool F8>
-__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_gate_add_ln_modulate(
+__global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_gate_add_ln_modulate(
     GateLnArgs a) {
   extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
