@@ -10,9 +10,11 @@ of 128), all in LOSSLESS mode:
   residual gate-add         residual, y [9216, 3072], per-batch gate
   Q/K RMSNorm + RoPE + joint QKV   merged QKV [2, 4096|512, 9216] -> 3 x [2, 4608, 24, 128]
 
-Inputs are resident in HBM before timing.  Two complete buffer sets are
-alternated step by step so that every kernel's operands were last touched
-about 0.9 GB of traffic earlier: the 256 MB Infinity Cache cannot serve them.
+Inputs are resident in HBM before timing.  Each kernel of a step reads row
+operands of its own (x and residual are copied per kernel that reads them),
+and two complete buffer sets are alternated step by step, so every kernel's
+operands were last touched about 1 GB of traffic earlier: the 256 MB Infinity
+Cache cannot serve them.
 Per-kernel durations come from HIP events that the kernel dispatches record
 themselves (dit_time_next_launch), on the launch stream.
 
@@ -128,6 +130,12 @@ class BufferSet:
     def __init__(self, blk, qkv, torch):
         self.x = to_dev(blk["x"], torch)
         self.res = to_dev(blk["residual"], torch)
+        # Kernels of one step that read the same tensor get copies of their
+        # own, so none of them finds its operands in the Infinity Cache
+        # because the kernel before it has just read them.
+        self.x_rms = to_dev(blk["x"], torch)
+        self.x_tanh = to_dev(blk["x"], torch)
+        self.res_tanh = to_dev(blk["residual"], torch)
         self.y = to_dev(blk["y"], torch)
         self.scale = to_dev(blk["scale"], torch)
         self.shift = to_dev(blk["shift"], torch)
@@ -170,10 +178,10 @@ def make_plans(m, s, mode):
     return {
         "ln_modulate": m.dit_ln_modulate(s.x, s.scale, s.shift, EPS, mode,
                                          out=s.out["ln_modulate"], prepare=True),
-        "rmsnorm_scale": m.dit_rmsnorm_scale(s.x, s.w, s.scale2, EPS, mode,
+        "rmsnorm_scale": m.dit_rmsnorm_scale(s.x_rms, s.w, s.scale2, EPS, mode,
                                              out=s.out["rmsnorm_scale"], prepare=True),
         "rmsnorm_tanh_residual": m.dit_rmsnorm_tanh_residual(
-            s.x, s.res, s.w, s.gate, EPS, mode, out=s.out["rmsnorm_tanh_residual"],
+            s.x_tanh, s.res_tanh, s.w, s.gate, EPS, mode, out=s.out["rmsnorm_tanh_residual"],
             prepare=True),
         "residual_gate_add": m.dit_residual_gate_add(s.res, s.y, s.gate, mode,
                                                      out=s.out["residual_gate_add"],
@@ -214,7 +222,7 @@ def time_alone(m, torch, sets, mode, reps=40):
 
 
 def time_producers(m, torch, sets, mode, steps):
-    """Each fused producer back to back over the two buffer sets (and, for
+    """Each fused producer back to back, rotating over the buffer sets (and, for
     the gated residual + LN producer, the unfused pair it replaces), each
     dispatch timed by its own events."""
     def run(calls):
@@ -226,7 +234,7 @@ def time_producers(m, torch, sets, mode, steps):
         for i in range(steps):
             for j, c in enumerate(calls):
                 m.dit_time_next_launch(*ev[i * len(calls) + j])
-                c[i % 2]()
+                c[i % len(c)]()
         torch.cuda.synchronize()
         us = [1000.0 * a.elapsed_time(b) for a, b in ev]
         return float(np.mean(us)) * len(calls), us
@@ -268,10 +276,11 @@ def time_producers(m, torch, sets, mode, steps):
                       rows_per_s=float("%.4g" % (ROWS / (us * 1e-6))))
     pair_us, _ = run([gate, ln])
     res["gate_add_ln_modulate"]["unfused_pair_us"] = round(pair_us, 2)
-    res["note"] = ("back to back; gate_add_ln_modulate replaces residual_gate_add + "
+    res["note"] = ("back to back over %d buffer sets; gate_add_ln_modulate replaces "
+                   "residual_gate_add + "
                    "ln_modulate (unfused_pair_us); fp8 variants add an E4M3 copy, scale %g; "
                    "qk_norm_rope_packed writes the destination-major [P, B, S, 3, H/P, 128] "
-                   "buffer for P = %d" % (FP8_SCALE, ULYSSES_P))
+                   "buffer for P = %d" % (len(sets), FP8_SCALE, ULYSSES_P))
     return res
 
 
@@ -661,7 +670,7 @@ def main():
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
         kernels_alone=time_alone(m, torch, sets + extra, args.mode),
-        producers=time_producers(m, torch, sets, args.mode, args.steps),
+        producers=time_producers(m, torch, sets + extra, args.mode, args.steps),
         wan720p=time_wan(m, torch, args.mode),
         copy_ceiling_gbs=copy_ceiling(m, torch),
     )

@@ -24,27 +24,42 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   const double qr = F8 ? 1.0 / (double)*a.fp8_scale : 1.0;   // E4M3 copy: 1 / scale
-  if (STAGED) {
-    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
-      const int64_t off = sp.m * a.mod_rs + 8 * v;
-      float g[8], s1[8], sh[8];
-      unpack8(load8(a.gate + off), g);
-      one_plus8(load8(a.scale + off), s1);
-      unpack8(load8(a.shift + off), sh);
-      stage_put(lds, v, g);
-      stage_put(lds + kRow, v, s1);
-      stage_put(lds + 2 * kRow, v, sh);
+  V8 rv[NC], yv[NC];
+  {
+    V8 gg[stage_iters<NC>()], gs[stage_iters<NC>()], gf[stage_iters<NC>()];
+    if (STAGED) {
+      const int64_t off = sp.m * a.mod_rs;
+      stage_fetch<NC>(gg, a.gate + off, dim);
+      stage_fetch<NC>(gs, a.scale + off, dim);
+      stage_fetch<NC>(gf, a.shift + off, dim);
     }
-    __syncthreads();
+    if (STAGED && sp.begin < sp.end) {
+      load_row<NC, kNtGate>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
+      load_row<NC, kNtGate>(yv, a.y + sp.begin * a.y_rs, lane, dim);
+    }
+    if (STAGED) {
+      stage_each<NC>(dim, [&](int i, int v) {
+        float g[8], s1[8], sh[8];
+        unpack8(gg[i], g);
+        one_plus8(gs[i], s1);
+        unpack8(gf[i], sh);
+        stage_put(lds, v, g);
+        stage_put(lds + kRow, v, s1);
+        stage_put(lds + 2 * kRow, v, sh);
+      });
+      __syncthreads();
+    }
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     const int64_t m = STAGED ? sp.m : r / a.per_mod;
     V8 xv[NC], sc[NC], sf[NC];
     {
-      V8 rv[NC], yv[NC], gv[NC];
-      load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
-      load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
+      V8 gv[NC];
+      if (!STAGED || r != sp.begin) {
+        load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
+        load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
+      }
       if (!STAGED) {
         load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
         load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);

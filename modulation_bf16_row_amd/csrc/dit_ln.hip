@@ -16,20 +16,26 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_ln_modulate(L
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   const double qr = F8 ? 1.0 / (double)*a.fp8_scale : 1.0;   // E4M3 copy: 1 / scale
+  V8 gs[stage_iters<NC>()], gf[stage_iters<NC>()], xv[NC];
   if (STAGED) {
-    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
+    stage_fetch<NC>(gs, a.scale + sp.m * a.mod_rs, dim);
+    stage_fetch<NC>(gf, a.shift + sp.m * a.mod_rs, dim);
+  }
+  if (STAGED && sp.begin < sp.end) load_row<NC, kNtLn>(xv, a.x + sp.begin * a.x_rs, lane, dim);
+  if (STAGED) {
+    stage_each<NC>(dim, [&](int i, int v) {
       float s1[8], sh[8];
-      one_plus8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s1);
-      unpack8(load8(a.shift + sp.m * a.mod_rs + 8 * v), sh);
+      one_plus8(gs[i], s1);
+      unpack8(gf[i], sh);
       stage_put(lds, v, s1);
       stage_put(lds + kRow, v, sh);
-    }
+    });
     __syncthreads();
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], sc[NC], sf[NC];
-    load_row<NC, kNtLn>(xv, a.x + r * a.x_rs, lane, dim);
+    V8 sc[NC], sf[NC];
+    if (!STAGED || r != sp.begin) load_row<NC, kNtLn>(xv, a.x + r * a.x_rs, lane, dim);
     if (!STAGED) {
       const int64_t m = r / a.per_mod;
       load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);

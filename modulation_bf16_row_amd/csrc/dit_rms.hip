@@ -38,14 +38,6 @@ __device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, float 
   round2(y0, y1);
 }
 
-// The RMSNorm weight as a staged row (every launch, both layouts).
-__device__ __forceinline__ void stage_weight(float4 *row, const uint16_t *weight, int dim) {
-  for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
-    float w[8];
-    unpack8(load8(weight + 8 * v), w);
-    stage_put(row, v, w);
-  }
-}
 
 // LDS: [0] = weight (always), [1] = scale (staged), binary32.
 template <int NC, int MODE, bool STAGED>
@@ -56,19 +48,24 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   if (sp.wg_empty) return;                                 // whole workgroup idle
-  stage_weight(lds, a.weight, dim);
-  if (STAGED) {
-    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
-      float s[8];
-      unpack8(load8(a.scale + sp.m * a.mod_rs + 8 * v), s);
-      stage_put(lds + kRow, v, s);
+  V8 gw[stage_iters<NC>()], gs[stage_iters<NC>()], xv[NC];
+  stage_fetch<NC>(gw, a.weight, dim);                      // weight: every launch
+  if (STAGED) stage_fetch<NC>(gs, a.scale + sp.m * a.mod_rs, dim);
+  if (STAGED && sp.begin < sp.end) load_row<NC, kNtRms>(xv, a.x + sp.begin * a.x_rs, lane, dim);
+  stage_each<NC>(dim, [&](int i, int v) {
+    float w[8];
+    unpack8(gw[i], w);
+    stage_put(lds, v, w);
+    if (STAGED) {
+      unpack8(gs[i], w);
+      stage_put(lds + kRow, v, w);
     }
-  }
+  });
   __syncthreads();
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], sc[NC];
-    load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
+    V8 sc[NC];
+    if (!STAGED || r != sp.begin) load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
     const int64_t m = STAGED ? sp.m : r / a.per_mod;
     if (!STAGED) load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
@@ -107,24 +104,36 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
   const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   if (sp.wg_empty) return;                                 // whole workgroup idle
+  V8 gw[stage_iters<NC>()], gg[stage_iters<NC>()], xv[NC], rv[NC];
+  stage_fetch<NC>(gw, a.weight, dim);                      // weight: every launch
+  if (STAGED) stage_fetch<NC>(gg, a.gate + sp.m * a.mod_rs, dim);
+  if (STAGED && sp.begin < sp.end) {
+    load_row<NC, kNtTanh>(xv, a.x + sp.begin * a.x_rs, lane, dim);
+    load_row<NC, kNtTanh>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
+  }
   tanh_table_fill(tab, threadIdx.x, kThreads);
-  stage_weight(lds, a.weight, dim);
+  stage_each<NC>(dim, [&](int i, int v) {
+    float w[8];
+    unpack8(gw[i], w);
+    stage_put(lds, v, w);
+  });
   __syncthreads();
   if (STAGED) {
-    for (int v = threadIdx.x; v < dim / 8; v += kThreads) {
-      const V8 g = load8(a.gate + sp.m * a.mod_rs + 8 * v);
+    stage_each<NC>(dim, [&](int i, int v) {
       float t[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = tanh_lookup(elem(g, j), tab);
+      for (int j = 0; j < 8; ++j) t[j] = tanh_lookup(elem(gg[i], j), tab);
       stage_put(lds + kRow, v, t);
-    }
+    });
     __syncthreads();
   }
 
   for (int64_t r = sp.begin; r < sp.end; ++r) {
-    V8 xv[NC], rv[NC], tau[NC];
-    load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
-    load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
+    V8 tau[NC];
+    if (!STAGED || r != sp.begin) {
+      load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
+      load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
+    }
     const int64_t m = STAGED ? sp.m : r / a.per_mod;
     if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
     const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);

@@ -132,6 +132,40 @@ __device__ __forceinline__ void stage_get(const float4 *row, int c, int lane, fl
   f[7] = b.w;
 }
 
+// The staging is split in two so that a workgroup's first rows are already
+// on their way from HBM while it stages: stage_fetch issues the global loads
+// of the vectors this thread converts (vector v = threadIdx.x + i kThreads,
+// i < stage_iters), the kernel then issues its first row's loads, and only
+// then converts the fetched vectors into LDS (stage_each).
+template <int NC>
+constexpr int stage_iters() {
+  return (NC * 64 + kThreads - 1) / kThreads;
+}
+
+template <int NC>
+__device__ __forceinline__ void stage_fetch(V8 (&buf)[stage_iters<NC>()], const uint16_t *src,
+                                            int dim) {
+#pragma unroll
+  for (int i = 0; i < stage_iters<NC>(); ++i) {
+    const int v = (int)threadIdx.x + i * kThreads;
+    if (v < dim / 8)
+      buf[i] = load8(src + 8 * v);
+    else
+      buf[i] = V8{{0u, 0u, 0u, 0u}};
+  }
+}
+
+// f(i, v) for each fetched vector i of this thread that lies in the row (v
+// is its vector index).
+template <int NC, class F>
+__device__ __forceinline__ void stage_each(int dim, F f) {
+#pragma unroll
+  for (int i = 0; i < stage_iters<NC>(); ++i) {
+    const int v = (int)threadIdx.x + i * kThreads;
+    if (v < dim / 8) f(i, v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row runs of this wave.
 // ---------------------------------------------------------------------------
