@@ -20,13 +20,13 @@ dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hip
 
 typedef enum {
   DIT_PROBE_ONE_PLUS = 0,   /* bf(1 + s)                                    */
-  DIT_PROBE_TANH = 1,       /* bf16 tanh of a bf16 gate from the binary32
-                               evaluation: with the rounding test and binary64
-                               re-evaluation (lossless), without it (fast)  */
+  /* 1 is reserved (rejected with DIT_ERR_INVALID)                           */
   DIT_PROBE_RMS_RSTD = 2,   /* bf(1 / sqrt(v)) of the RMSNorm chain (mode)   */
-  DIT_PROBE_TANH_TABLE = 3  /* bf16 tanh as dit_rmsnorm_tanh_residual takes it
-                               (LDS table filled from the lossless op 1;
-                               mode-independent)                            */
+  DIT_PROBE_TANH_TABLE = 3  /* bf16 tanh of a bf16 gate as
+                               dit_rmsnorm_tanh_residual takes it: the
+                               identity below 2^-4, +-1 from 3.5, else the
+                               library's table of correctly rounded values
+                               (mode-independent)                           */
 } dit_probe_unary_t;
 
 /* out[i] = op(in[i]) on bf16 bit patterns. */

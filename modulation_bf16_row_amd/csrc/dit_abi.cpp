@@ -619,7 +619,7 @@ dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hip
 
 dit_status_t dit_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
                              hipStream_t stream) {
-  if (op < DIT_PROBE_ONE_PLUS || op > DIT_PROBE_TANH_TABLE)
+  if (op != DIT_PROBE_ONE_PLUS && op != DIT_PROBE_RMS_RSTD && op != DIT_PROBE_TANH_TABLE)
     return fail(DIT_ERR_INVALID, "bad op");
   if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
     return fail(DIT_ERR_INVALID, "unknown mode");

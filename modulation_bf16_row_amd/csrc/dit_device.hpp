@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dit_tanh_table.hpp"
+
 namespace dit {
 
 enum { kLossless = 0, kFast = 1 };
@@ -39,20 +41,6 @@ __device__ __forceinline__ void round2(float &a, float &b) {
 }
 
 __device__ __forceinline__ float round1(float a) { return lo(pack(a, a)); }
-
-// Correctly rounded bf16 of a binary64 value, via a binary32 value rounded to
-// odd (truncate toward zero and set the last bit if anything was dropped):
-// rounding to odd with 24 bits then to nearest with 8 bits equals one
-// rounding to nearest with 8 bits, since 24 >= 8 + 2.
-__device__ __forceinline__ float round_f64(double v) {
-  float f = (float)v;                           // nearest
-  if ((double)f != v && f == f) {
-    uint32_t u = __float_as_uint(f);
-    if (fabs((double)f) > fabs(v)) u -= 1;      // step back toward zero
-    f = __uint_as_float(u | 1u);                // sticky bit: odd
-  }
-  return round1(f);
-}
 
 // ---------------------------------------------------------------------------
 // Fixed reduction trees.  Lane l adds the partial of lane l^m for each m;
@@ -124,87 +112,6 @@ __device__ __forceinline__ float group16_sum(float p) {
 }
 
 // ---------------------------------------------------------------------------
-// tanh of a bf16 gate, rounded to bf16.
-//
-// binary32 evaluation of tanh(a), a = |g| (odd symmetry restores the sign):
-//   a < 0.3:      the Taylor series a + a^3 * P(a^2) through a^13, with the
-//                 coefficients 2^2n (2^2n - 1) B_2n / (2n)! of the expansion
-//                 (-1/3, 2/15, -17/315, 62/2835, -1382/155925,
-//                 21844/6081075); the first omitted term is below 2^-33
-//                 relative at a = 0.3;
-//   0.3 <= a < 4: 1 - 2 / (2^(2a log2 e) + 1) with the hardware exp2 and
-//                 reciprocal (no cancellation since the exponential >= 1.8);
-//   a >= 4:       the bf16 result is 1.
-// Its error is a few binary32 ulps.  LOSSLESS adds Ziv's rounding test: when
-// the binary32 value lies within kZivUlps ulps of a bf16 rounding boundary
-// (its low 16 bits near 0x8000), tanh is re-evaluated in binary64 and
-// rounded once.  The result is then the correctly rounded bf16 of tanh(g)
-// for every one of the 65536 inputs, which the exhaustive device test
-// checks.  FAST mode skips the test (within one bf16 step).
-// ---------------------------------------------------------------------------
-constexpr int kZivUlps = 16;
-
-__device__ __forceinline__ float tanh_f32(float a) {
-  if (a < 0.3f) {
-    const float s = a * a;
-    float p = fmaf(s, 21844.0f / 6081075.0f, -1382.0f / 155925.0f);
-    p = fmaf(s, p, 62.0f / 2835.0f);
-    p = fmaf(s, p, -17.0f / 315.0f);
-    p = fmaf(s, p, 2.0f / 15.0f);
-    p = fmaf(s, p, -1.0f / 3.0f);
-    return fmaf(a * s, p, a);
-  }
-  const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);   // 2 log2(e)
-  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
-}
-
-// bf16 tanh of g from the binary32 evaluation.  In LOSSLESS mode, when that
-// value is too close to a bf16 rounding boundary, bit `bit` of `need` is set
-// and the caller must replace the result with tanh_fix().
-template <int MODE>
-__device__ __forceinline__ float tanh_try(float g, uint32_t &need, int bit) {
-  const float a = fabsf(g);
-  float r;
-  if (!(a < 4.0f)) {
-    r = (a == a) ? 1.0f : a + a;                // saturate; NaN stays NaN (quiet)
-  } else {
-    const float t = tanh_f32(a);
-    if (MODE == kLossless) {
-      const int low = (int)(__float_as_uint(t) & 0xFFFFu);
-      if (abs(low - 0x8000) <= kZivUlps) need |= 1u << bit;
-    }
-    r = round1(t);
-  }
-  return copysignf(r, g);
-}
-
-// Re-evaluates in binary64 (rounded once) the elements of t flagged in need;
-// gate(j) returns gate j.  One inline copy of the binary64 evaluation serves
-// all N elements: the flagged element is fetched, evaluated and written back
-// in a loop.
-template <int N, class Gate>
-__device__ __forceinline__ void tanh_fix(float (&t)[N], uint32_t need, Gate gate) {
-  while (need) {
-    const int j = __builtin_ctz(need);
-    need &= need - 1;
-    const float gj = gate(j);
-    const float r = copysignf(round_f64(tanh((double)fabsf(gj))), gj);
-#pragma unroll
-    for (int k = 0; k < N; ++k) t[k] = (j == k) ? r : t[k];
-  }
-}
-
-// tanh of one bf16 gate, rounded to bf16.
-template <int MODE>
-__device__ __forceinline__ float tanh_bf16(float g) {
-  float t[1] = {0.0f};
-  uint32_t need = 0;
-  t[0] = tanh_try<MODE>(g, need, 0);
-  if (MODE == kLossless && need) tanh_fix<1>(t, need, [&](int) { return g; });
-  return t[0];
-}
-
-// ---------------------------------------------------------------------------
 // tanh of a bf16 gate by table, as the row kernels use it (both modes).
 //   |g| < 2^-4:   bf(tanh g) = g, since the relative change of tanh, about
 //                 g^2 / 3 < 2^-9.5, is below half a bf16 spacing (>= 2^-9
@@ -213,19 +120,29 @@ __device__ __forceinline__ float tanh_bf16(float g) {
 //   |g| >= 3.5:   +-1, since tanh(3.5) > 1 - 2^-9, the midpoint below 1;
 //                 infinities give +-1, NaN stays NaN (quiet);
 //   otherwise:    one of the 736 magnitudes with bf16 codes 0x3D80..0x405F,
-//                 looked up in a table of their correctly rounded tanh,
-//                 filled from tanh_bf16<kLossless>; the sign is restored.
-// The exhaustive device test checks every one of the 65536 inputs.
+//                 looked up in a table of their correctly rounded tanh
+//                 (dit_tanh_table.hpp, written by gen_tanh_table.py from
+//                 80-digit decimal arithmetic); the sign is restored.
+// Each workgroup copies the 1472-byte table from global memory (an L2 hit
+// after the first workgroups) into LDS.  The exhaustive device test checks
+// every one of the 65536 inputs.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kTanhTabLo = 0x3D80u, kTanhTabHi = 0x4060u;
 constexpr int kTanhTabN = (int)(kTanhTabHi - kTanhTabLo);             // 736
 constexpr int kTanhTabVecs = (kTanhTabN * 2 + 15) / 16;               // uint4s
+static_assert(kTanhTabN == kTanhTabEntries && kTanhTabN % 8 == 0, "tanh table size");
 
-__device__ __forceinline__ void tanh_table_fill(uint16_t *tab, int tid, int nthreads) {
-  for (int i = tid; i < kTanhTabN; i += nthreads) {
-    const float r = tanh_bf16<kLossless>(__uint_as_float((kTanhTabLo + (uint32_t)i) << 16));
-    tab[i] = (uint16_t)(__float_as_uint(r) >> 16);
-  }
+// The copy in two halves, so that a kernel can issue other loads between
+// them: thread tid < kTanhTabVecs fetches 16 bytes of the table, then puts
+// them into LDS (tab: 16-byte aligned, kTanhTabVecs uint4s).  The workgroup
+// needs at least kTanhTabVecs threads.
+__device__ __forceinline__ uint4 tanh_table_fetch(int tid) {
+  return tid < kTanhTabVecs ? reinterpret_cast<const uint4 *>(kTanhTabGlobal)[tid]
+                            : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ void tanh_table_put(uint16_t *tab, int tid, uint4 v) {
+  if (tid < kTanhTabVecs) reinterpret_cast<uint4 *>(tab)[tid] = v;
 }
 
 // g is a bf16 value (low 16 bits zero).  The table index is clamped, so the

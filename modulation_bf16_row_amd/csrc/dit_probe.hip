@@ -12,14 +12,16 @@ __global__ void k_probe_bf16_round(uint16_t *out, const float *in, int64_t n) {
   if (i < n) out[i] = (uint16_t)(pack(in[i], 0.0f) & 0xFFFFu);
 }
 
-// op 0: bf(1 + s); op 1: tanh to bf16; op 2: bf(1 / sqrt(v)) as in RMSNorm;
-// op 3: tanh through the row kernels' LDS table (filled by each workgroup).
+// op 0: bf(1 + s); op 2: bf(1 / sqrt(v)) as in RMSNorm; op 3: tanh through
+// the row kernels' LDS table (copied by each workgroup).  (op 1, a binary32
+// evaluation of tanh, is no longer part of the library; the host rejects it.)
 template <int MODE>
 __global__ __launch_bounds__(256) void k_probe_unary(int op, uint16_t *out, const uint16_t *in,
                                                      int64_t n) {
-  __shared__ uint16_t tab[kTanhTabN];
+  __shared__ __attribute__((aligned(16))) uint16_t tab[kTanhTabN];
+  static_assert(256 >= kTanhTabVecs, "one workgroup copies the tanh table in one pass");
   if (op == 3) {                                 // op is uniform: every thread reaches the barrier
-    tanh_table_fill(tab, threadIdx.x, blockDim.x);
+    tanh_table_put(tab, threadIdx.x, tanh_table_fetch(threadIdx.x));
     __syncthreads();
   }
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -28,8 +30,6 @@ __global__ __launch_bounds__(256) void k_probe_unary(int op, uint16_t *out, cons
   float r;
   if (op == 0)
     r = round1(1.0f + v);
-  else if (op == 1)
-    r = tanh_bf16<MODE>(v);
   else if (op == 2)
     r = round1(rsqrt_mode<MODE>(v));
   else

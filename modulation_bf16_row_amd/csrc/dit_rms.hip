@@ -105,13 +105,14 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
                          : spans(a.rows, a.rows_per_wave);
   if (sp.wg_empty) return;                                 // whole workgroup idle
   V8 gw[stage_iters<NC>()], gg[stage_iters<NC>()], xv[NC], rv[NC];
+  const uint4 tv = tanh_table_fetch(threadIdx.x);
   stage_fetch<NC>(gw, a.weight, dim);                      // weight: every launch
   if (STAGED) stage_fetch<NC>(gg, a.gate + sp.m * a.mod_rs, dim);
   if (STAGED && sp.begin < sp.end) {
     load_row<NC, kNtTanh>(xv, a.x + sp.begin * a.x_rs, lane, dim);
     load_row<NC, kNtTanh>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
   }
-  tanh_table_fill(tab, threadIdx.x, kThreads);
+  tanh_table_put(tab, threadIdx.x, tv);
   stage_each<NC>(dim, [&](int i, int v) {
     float w[8];
     unpack8(gw[i], w);

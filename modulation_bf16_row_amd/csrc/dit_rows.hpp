@@ -45,6 +45,7 @@ namespace dit {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 64 * kWavesPerBlock;
+static_assert(kThreads >= kTanhTabVecs, "one workgroup copies the tanh table in one pass");
 
 // Load policy of the streamed row inputs, per kernel, as measured on MI355X
 // (Qwen-Image and Wan shapes): the nontemporal policy helps the kernels that

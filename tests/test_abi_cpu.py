@@ -69,6 +69,7 @@ def stub(tmp_path_factory):
     lib.dit_gate_add_ln_modulate_fp8.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                                  vp, vp, i64, i64, i64, i64, f32, vp, cint, vp]
     lib.dit_probe_fp8.argtypes = [cint, vp, vp, i64, vp, vp]
+    lib.dit_probe_unary.argtypes = [cint, vp, vp, i64, cint, vp]
     lib.dit_wan_modulation_table.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
     return lib
 
@@ -254,6 +255,15 @@ def test_probe_fp8_guards(stub):
     assert stub.dit_probe_fp8(1, Q8, X, 16, None, None) == INVALID    # quant needs the scale
     assert stub.dit_probe_fp8(0, Q8, X, 16, None, None) == OK
     assert stub.dit_probe_fp8(0, Q8, X, 0, None, None) == OK
+
+
+def test_probe_unary_guards(stub):
+    f = stub.dit_probe_unary
+    assert f(1, OUT, X, 16, 0, None) == INVALID     # reserved (no binary32 tanh evaluation)
+    assert f(4, OUT, X, 16, 0, None) == INVALID
+    assert f(0, OUT, X, 16, 2, None) == INVALID     # mode
+    for op in (0, 2, 3):
+        assert f(op, OUT, X, 16, 1, None) == OK
 
 
 def test_wan_modulation_table_guards(stub):
