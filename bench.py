@@ -558,6 +558,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mode", default="lossless", choices=["lossless", "fast"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step and its kernels only (no kernels_alone, producers, "
+                         "Wan shapes, copy ceiling or oracle leg): a kernel trace of this run "
+                         "holds only in-step dispatches of the step kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -648,7 +652,7 @@ def main():
 
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    extra = [BufferSet(blk, qkv, torch), BufferSet(blk, qkv, torch)]   # for time_alone
+    extra = [] if args.only_step else [BufferSet(blk, qkv, torch), BufferSet(blk, qkv, torch)]
     dom = "ln_modulate"
     achieved = per_kernel[dom]["gbs"]
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
@@ -669,12 +673,14 @@ def main():
         **{"kernels_" + other: per_kernel_other},
         eager_ms_per_step=round(eager_ms_step, 4),
         kernel_sum_ms_per_step=round(sum(k_us.values()) / 1000.0, 4),
-        kernels_alone=time_alone(m, torch, sets + extra, args.mode),
-        producers=time_producers(m, torch, sets + extra, args.mode, args.steps),
-        wan720p=time_wan(m, torch, args.mode),
-        copy_ceiling_gbs=copy_ceiling(m, torch),
     )
-    if not args.no_cpu:
+    if not args.only_step:
+        result.update(
+            kernels_alone=time_alone(m, torch, sets + extra, args.mode),
+            producers=time_producers(m, torch, sets + extra, args.mode, args.steps),
+            wan720p=time_wan(m, torch, args.mode),
+            copy_ceiling_gbs=copy_ceiling(m, torch))
+    if not args.no_cpu and not args.only_step:
         gpu_out = {k: sets[0].out[k].cpu().view(torch.int16).numpy().view(np.uint16)
                    for k in ROW_KERNELS}
         gpu_out["qk_norm_rope"] = [t.cpu().view(torch.int16).numpy().view(np.uint16)

@@ -67,8 +67,10 @@ def unit_files(source):
 def kernel_source_hash(source=None):
     """Hash of the code (comments and whitespace excluded) of the kernel
     sources: of one translation unit (`source`, e.g. "dit_ln.hip", and the
-    headers it includes) or, with no argument, of every file in csrc/."""
-    names = unit_files(source) if source else sorted(os.listdir(CSRC))
+    headers it includes) or, with no argument, of every C++/HIP source in
+    csrc/."""
+    names = unit_files(source) if source else sorted(
+        n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp", ".cpp", ".h")))
     h = hashlib.sha256()
     for name in names:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:

@@ -2,7 +2,8 @@
 writes, and every entry equals the oracle's correctly rounded bf16 tanh.
 
 The two sides compute tanh independently: the generator in 80-digit decimal
-arithmetic, the oracle in C (long double with a rounding-boundary check).
+arithmetic, the oracle in C from the binary64 tanh rounded once to bf16
+(itself pinned against long double on all 65536 inputs).
 The device lookup around the table (identity below 2^-4, +-1 from 3.5, NaN)
 is checked over all 65536 inputs by the GPU primitive tests."""
 import os
