@@ -35,7 +35,7 @@ Wan 720p block's kernels (75600 x 5120, per-token modulation, the modulation
 table) are timed on their own, the latter with 8 sampled rows of each output
 checked against the oracle.
 The CPU baseline runs the oracle (plain C) over full steps on the host,
-single-threaded (the reported value: steps repeated to about 10 s of CPU
+single-threaded (the reported value: steps repeated to about 12 s of CPU
 work, per-epilogue medians) and on all threads of the process's CPU share
 (row blocks in parallel), and compares the GPU's outputs with it bit for
 bit.
@@ -497,7 +497,7 @@ def _same(a, b):
     return bool(np.array_equal(a, b))
 
 
-def cpu_baseline(blk, qkv, gpu_out, budget_s=9.0, max_runs=5):
+def cpu_baseline(blk, qkv, gpu_out, budget_s=11.0, max_runs=6):
     """The oracle over full steps on the host: one thread (the reported value;
     steps repeated until about `budget_s` of CPU work, per-epilogue medians)
     and all threads of this process's CPU share (row blocks in parallel,
