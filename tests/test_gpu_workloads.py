@@ -10,8 +10,9 @@ benchmark times, plus FAST-mode tolerances and the 50-iteration chain.
   oracle on a sample of rows (rows are independent), plus the first and last
   rows.
 - FAST mode against LOSSLESS: at most 2 bf16 steps, measured in steps of the
-  magnitude entering the last rounding, and >= 99.9% of elements within 1
-  step (literal); the literal maximum is printed.
+  magnitude entering the last rounding (LN + modulate on sampled rows; Q and
+  K everywhere, from the head norm and the cos/sin tables), and >= 99.9% of
+  elements within 1 step (literal); the literal maximum is printed.
 - Chain: 50 iterations of LN+modulate -> gate-add -> RMSNorm-scale fed back;
   LOSSLESS equals the oracle at every iteration on sampled rows; FAST stays
   >= 40 dB PSNR against LOSSLESS after 50 iterations.
@@ -198,9 +199,32 @@ def test_fast_mode_tolerances(qwen, qkv):
     say("FAST vs LOSSLESS, qwen qkv")
     ql = _qkv_run(qkv, "lossless")
     qf = _qkv_run(qkv, "fast")
-    for name, a, b in zip("qk", qf[:2], ql[:2]):
-        lit, frac1, _ = _fast_report("qk_norm_rope " + name, a, b)
+    # Magnitudes entering RoPE's last rounding, max(|a c|, |b z|) for o_2i and
+    # max(|a z|, |b c|) for o_2i+1, from the LOSSLESS head norm u = (a, b):
+    # the oracle with an identity rotation (cos 1, sin 0) returns u itself.
+    q = qkv
+    H = q["heads"]
+    tq, tk, tv = _qkv_views(q["txt_qkv"], H)
+    iq, ik, iv = _qkv_views(q["img_qkv"], H)
+    u = oracle.qk_norm_rope(
+        dict(q=tq, k=tk, v=tv, q_weight=q["txt_q_weight"], k_weight=q["txt_k_weight"]),
+        dict(q=iq, k=ik, v=iv, q_weight=q["img_q_weight"], k_weight=q["img_k_weight"]),
+        np.ones_like(q["cos"]), np.zeros_like(q["sin"]), q["eps"])
+    c = q["cos"].astype(np.float64)[None, :, None, :]
+    z = q["sin"].astype(np.float64)[None, :, None, :]
+    for i, name in enumerate("qk"):
+        lit, frac1, _ = _fast_report("qk_norm_rope " + name, qf[i], ql[i])
         assert frac1 >= 0.999
+        uv = value_of_bf16(u[i]).reshape(*u[i].shape[:3], -1, 2)
+        ua, ub = uv[..., 0], uv[..., 1]
+        mag = np.empty_like(uv)
+        mag[..., 0] = np.maximum(np.abs(ua * c), np.abs(ub * z))
+        mag[..., 1] = np.maximum(np.abs(ua * z), np.abs(ub * c))
+        del uv, ua, ub
+        _, _, scaled = _fast_report("qk_norm_rope " + name + " (scaled)", qf[i], ql[i],
+                                    mag.reshape(qf[i].shape))
+        assert scaled <= 2.0
+        del mag
     assert np.array_equal(qf[2], ql[2])
 
 
