@@ -51,15 +51,12 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
     }
   }
 
-  for (int64_t r = sp.begin; r < sp.end; ++r) {
+  // One row whose residual and y are in rv and yv.
+  auto row = [&](int64_t r) {
     const int64_t m = STAGED ? sp.m : r / a.per_mod;
     V8 xv[NC], sc[NC], sf[NC];
     {
       V8 gv[NC];
-      if (!STAGED || r != sp.begin) {
-        load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
-        load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
-      }
       if (!STAGED) {
         load_mod_row<NC>(gv, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
         load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
@@ -105,6 +102,15 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
                                 unpack8(sf[c], sh);
                               });
     }
+  };
+  // The staged layout's first row was loaded before the staging; it is
+  // handled apart from the loop so that rv and yv are not carried around it.
+  int64_t r = sp.begin;
+  if (STAGED && r < sp.end) row(r++);
+  for (; r < sp.end; ++r) {
+    load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
+    load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
+    row(r);
   }
 }
 
