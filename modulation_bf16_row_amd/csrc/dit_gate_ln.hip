@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
     }
     if (STAGED && sp.begin < sp.end) {
       load_row<NC, kNtGate>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
-      load_row<NC, kNtGate>(yv, a.y + sp.begin * a.y_rs, lane, dim);
+      load_row<NC, kNtGateLnY>(yv, a.y + sp.begin * a.y_rs, lane, dim);
     }
     if (STAGED) {
       stage_each<NC>(dim, [&](int i, int v) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
   if (STAGED && r < sp.end) row(r++);
   for (; r < sp.end; ++r) {
     load_row<NC, kNtGate>(rv, a.residual + r * a.res_rs, lane, dim);
-    load_row<NC, kNtGate>(yv, a.y + r * a.y_rs, lane, dim);
+    load_row<NC, kNtGateLnY>(yv, a.y + r * a.y_rs, lane, dim);
     row(r);
   }
 }

@@ -50,11 +50,18 @@ static_assert(kThreads >= kTanhTabVecs, "one workgroup copies the tanh table in 
 // Load policy of the streamed row inputs, per kernel, as measured on MI355X
 // (Qwen-Image and Wan shapes): the nontemporal policy helps the kernels that
 // read two or more row streams and slows the single-stream norms.
+// The gated residual + LN producer reads its residual nontemporal and y with
+// the default policy (kNtGateLnY): 38.0 against 41.0 us at the Qwen-Image
+// shape, in a DiT-order sequence with the QKV and RMSNorm epilogues after it,
+// which it does not slow.  The same split in the standalone gate-add and
+// tanh-residual made those faster back to back but slowed LN and RMS-scale in
+// the five-kernel step by ~4 us each, so they keep both streams nontemporal.
 #ifdef DIT_NO_NT_LOAD
 constexpr bool kNtLn = false, kNtRms = false, kNtTanh = false, kNtGate = false, kNtMod = false;
 #else
 constexpr bool kNtLn = false, kNtRms = false, kNtTanh = true, kNtGate = true, kNtMod = false;
 #endif
+constexpr bool kNtGateLnY = false;
 
 // Register budget: at least W6 waves per SIMD at dim <= 3072 (NC <= 6),
 // scaled down in proportion (rounded) for longer rows.
