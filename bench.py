@@ -543,7 +543,8 @@ def _bf16_nan(h):
 
 
 def _bf16_values(h):
-    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns
+        return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def fast_mode_report(m, torch, s, chain_iters=50):
