@@ -596,26 +596,32 @@ def fast_mode_report(m, torch, s, chain_iters=50):
 
 
 def copy_ceiling(m, torch, nbytes=1 << 30, reps=5):
-    """Practical HBM ceiling: the library's streaming-copy probe (128-bit
-    accesses, nontemporal loads and stores) over a 1 GiB buffer, 2 GiB moved
-    per copy, far beyond the Infinity Cache; GB/s of read + write.  These
-    dispatches of known size also calibrate the memory counters."""
+    """Practical HBM ceilings: the library's streaming-copy probe over a
+    1 GiB buffer, 2 GiB moved per copy, far beyond the Infinity Cache; GB/s of
+    read + write, with nontemporal loads and stores.  Two layouts: one 16-byte
+    vector per lane in one-shot 64-thread workgroups (the flat kernels'
+    layout; the ceiling), and a grid-stride loop with 1 KiB per wave
+    instruction (whose dispatches of known size also calibrate the memory
+    counters)."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    m.dit_probe_copy(dst, src, 3)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    for a, b in evs:
-        m.dit_time_next_launch(a, b)
-        m.dit_probe_copy(dst, src, 3)
-    torch.cuda.synchronize()
-    sec = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    res = {}
+    for flags in (7, 3):
+        m.dit_probe_copy(dst, src, flags)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            m.dit_time_next_launch(a, b)
+            m.dit_probe_copy(dst, src, flags)
+        torch.cuda.synchronize()
+        sec = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        res[flags] = round(2 * nbytes / sec / 1e9, 1)
     del src, dst
-    return round(2 * nbytes / sec / 1e9, 1)
+    return res[7], res[3]
 
 
 def main():
@@ -746,8 +752,9 @@ def main():
             kernels_alone=time_alone(m, torch, sets + extra, args.mode),
             producers=time_producers(m, torch, sets + extra, args.mode, args.steps),
             wan720p=time_wan(m, torch, args.mode),
-            copy_ceiling_gbs=copy_ceiling(m, torch),
+            copy_ceiling_gbs=None, copy_grid_stride_gbs=None,
             fast_mode=fast_mode_report(m, torch, sets[0]))
+        result["copy_ceiling_gbs"], result["copy_grid_stride_gbs"] = copy_ceiling(m, torch)
     if not args.no_cpu and not args.only_step:
         gpu_out = {k: sets[0].out[k].cpu().view(torch.int16).numpy().view(np.uint16)
                    for k in ROW_KERNELS}

@@ -55,7 +55,8 @@ dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t
  * buffers) with the epilogues' access pattern: 128-bit accesses, 1 KiB
  * contiguous per wave instruction.  Used as the practical HBM ceiling and to
  * calibrate memory counters.  flags bit 0: nontemporal loads; bit 1:
- * nontemporal stores. */
+ * nontemporal stores; bit 2: the flat kernels' layout instead (one 16-byte
+ * vector per lane, one-shot 64-thread workgroups; bytes / 1024 < 2^31). */
 dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
                             hipStream_t stream);
 

@@ -656,11 +656,13 @@ dit_status_t dit_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, cons
 dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
                             hipStream_t stream) {
   if (bytes < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (flags < 0 || flags > 3) return fail(DIT_ERR_INVALID, "flags must be in [0, 3]");
+  if (flags < 0 || flags > 7) return fail(DIT_ERR_INVALID, "flags must be in [0, 7]");
   if (bytes == 0) return DIT_OK;
   if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
   if (bytes % 16 != 0 || !aligned16(out) || !aligned16(in))
     return fail(DIT_ERR_UNSUPPORTED, "bytes and pointers must be multiples of 16");
+  if ((flags & 4) && bytes / 16 / 64 >= 0x7FFFFFFF)
+    return fail(DIT_ERR_UNSUPPORTED, "too many vectors for the one-shot layout");
   if (spans_overlap(Span{reinterpret_cast<uintptr_t>(out), 0, 1, bytes},
                     Span{reinterpret_cast<uintptr_t>(in), 0, 1, bytes}))
     return fail(DIT_ERR_INVALID, "buffers overlap");

@@ -106,14 +106,37 @@ __global__ __launch_bounds__(256) void k_probe_copy(u32x4 *out, const u32x4 *in,
   }
 }
 
+// The flat kernels' layout: one 16-byte vector per lane, one-shot 64-thread
+// workgroups.
+template <int FLAGS>
+__global__ __launch_bounds__(64) void k_probe_stream(u32x4 *out, const u32x4 *in, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= n) return;
+  const u32x4 v = (FLAGS & 1) ? __builtin_nontemporal_load(in + i) : in[i];
+  if (FLAGS & 2)
+    __builtin_nontemporal_store(v, out + i);
+  else
+    out[i] = v;
+}
+
 static dim3 flat_grid(int64_t n, int block) { return dim3((unsigned)((n + block - 1) / block)); }
 
 hipError_t launch_probe_copy(void *out, const void *in, int64_t n16, int flags, hipStream_t s) {
+  u32x4 *o = static_cast<u32x4 *>(out);
+  const u32x4 *i = static_cast<const u32x4 *>(in);
+  if (flags & 4) {
+    const dim3 grid = flat_grid(n16, 64);
+    switch (flags & 3) {
+      case 0: DIT_LAUNCH(k_probe_stream<0>, grid, dim3(64), 0, s, o, i, n16); break;
+      case 1: DIT_LAUNCH(k_probe_stream<1>, grid, dim3(64), 0, s, o, i, n16); break;
+      case 2: DIT_LAUNCH(k_probe_stream<2>, grid, dim3(64), 0, s, o, i, n16); break;
+      default: DIT_LAUNCH(k_probe_stream<3>, grid, dim3(64), 0, s, o, i, n16); break;
+    }
+    return hipGetLastError();
+  }
   int64_t blocks = (n16 + 1023) / 1024;
   if (blocks > 256 * 16) blocks = 256 * 16;
   const dim3 grid((unsigned)blocks);
-  u32x4 *o = static_cast<u32x4 *>(out);
-  const u32x4 *i = static_cast<const u32x4 *>(in);
   switch (flags & 3) {
     case 0: DIT_LAUNCH(k_probe_copy<0>, grid, dim3(256), 0, s, o, i, n16); break;
     case 1: DIT_LAUNCH(k_probe_copy<1>, grid, dim3(256), 0, s, o, i, n16); break;

@@ -70,6 +70,7 @@ def stub(tmp_path_factory):
                                                  vp, vp, i64, i64, i64, i64, f32, vp, cint, vp]
     lib.dit_probe_fp8.argtypes = [cint, vp, vp, i64, vp, vp]
     lib.dit_probe_unary.argtypes = [cint, vp, vp, i64, cint, vp]
+    lib.dit_probe_copy.argtypes = [vp, vp, i64, cint, vp]
     lib.dit_wan_modulation_table.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
     return lib
 
@@ -264,6 +265,17 @@ def test_probe_unary_guards(stub):
     assert f(0, OUT, X, 16, 2, None) == INVALID     # mode
     for op in (0, 2, 3):
         assert f(op, OUT, X, 16, 1, None) == OK
+
+
+def test_probe_copy_guards(stub):
+    f = stub.dit_probe_copy
+    for flags in range(8):                          # bit 2: the flat layout
+        assert f(OUT, X, 1024, flags, None) == OK
+    assert f(OUT, X, 1024, 8, None) == INVALID
+    assert f(OUT, X, 1024, -1, None) == INVALID
+    assert f(OUT, X, 24, 7, None) == UNSUPPORTED     # not a multiple of 16 bytes
+    assert f(OUT, OUT + 512, 1024, 7, None) == INVALID   # overlapping buffers
+    assert f(OUT, X, 0, 7, None) == OK
 
 
 def test_wan_modulation_table_guards(stub):

@@ -88,6 +88,21 @@ def test_rms_rstd_fast_within_one_step():
     assert ulp_distance(got[fin], ref[fin]).max() <= 1
 
 
+@pytest.mark.parametrize("flags", range(8))
+def test_copy_probe_copies_in_both_layouts(flags):
+    """The streaming-copy probe (the bench's ceiling and the counters'
+    calibration) moves every byte, in the grid-stride and the flat layout, on
+    sizes that leave partial workgroups."""
+    say("copy probe flags", flags)
+    for n in (8, 8 * 1000 + 8, 8 * 64 * 1024 * 3 + 8 * 17):
+        src = torch.arange(n, dtype=torch.int32, device="cuda:0").to(torch.int16).view(
+            torch.bfloat16)
+        dst = torch.zeros_like(src)
+        m().dit_probe_copy(dst, src, flags)
+        torch.cuda.synchronize()
+        assert torch.equal(dst.view(torch.int16), src.view(torch.int16)), (flags, n)
+
+
 def _f32_cases(n, seed):
     rng = np.random.default_rng(seed)
     bits = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
