@@ -133,6 +133,30 @@ MUTANTS = {
         "return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
         "return (uint16_t)((u + 0x8000u) >> 16);",
         ["test_bf16_round_edges_vs_fractions"]),
+    "RMSNorm y1 not rounded": (
+        "float y1 = bfv(orc_bf16_value(x[i]) * rv);",
+        "float y1 = orc_bf16_value(x[i]) * rv;",
+        ["test_rms_y1_rounded_before_the_weight"]),
+    "RMSNorm rstd from the unrounded ms + eps": (
+        "uint16_t rstd = orc_rms_rstd(v);",
+        "uint16_t rstd = orc_bf16_round(1.0f / sqrtf(orc_bf16_value(ms) + eps));",
+        ["test_rms_rstd_taken_from_the_rounded_mean_square_plus_eps"]),
+    "QK head x * rho not rounded": (
+        "float n = bfv(orc_bf16_value(x[i]) * rho);",
+        "float n = orc_bf16_value(x[i]) * rho;",
+        ["test_qk_head_normalized_value_rounded_before_the_weight"]),
+    "RoPE first output fused": (
+        "o[2 * i] = orc_bf16_round(a * c[i] - b * z[i]);",
+        "o[2 * i] = orc_bf16_round(fmaf(a, c[i], -(b * z[i])));",
+        ["test_qk_head_rope_products_rounded_separately"]),
+    "RoPE second output fused": (
+        "o[2 * i + 1] = orc_bf16_round(a * z[i] + b * c[i]);",
+        "o[2 * i + 1] = orc_bf16_round(fmaf(a, z[i], b * c[i]));",
+        ["test_qk_head_rope_products_rounded_separately"]),
+    "LayerNorm divides by sigma": (
+        "for (int64_t i = 0; i < D; ++i) n[i] = orc_bf16_round(d[i] * rho);",
+        "for (int64_t i = 0; i < D; ++i) n[i] = orc_bf16_round(d[i] / sqrtf(var + eps));",
+        ["test_ln_normalizes_by_multiplying_with_rho"]),
 }
 
 

@@ -300,6 +300,37 @@ def test_ln_scale_minus_one_gives_shift():
     assert np.array_equal(oracle.ln_modulate(x, scale, shift), np.repeat(shift, 8, axis=0))
 
 
+def test_ln_normalizes_by_multiplying_with_rho():
+    """LayerNorm normalizes as d * rho with rho = 1 / sqrt(var + eps) rounded
+    to binary32 first (the "RSQ path" of page "基于Agent的SGLang扩散模型Kernel
+    优化实践", section "数学等价不代表结果完全一致"), not as d / sqrt(var + eps).
+    Hand-derived row, D = 8, eps = 1e-6 (binary32 0x358637BD):
+    x = (p, -p, q, -q, r, -r, s, -s) with p, q, r, s = 1.046875, 1.9453125,
+    1.6953125, 1.078125.  The mean is exactly 0 and d = x; the squares are
+    exact and sum to 17.83325195..., so var = 2.229156494140625 (0x400EAA80)
+    exactly; var + eps rounds to 0x400EAA84; its square root to
+    sigma = 0x3FBF1BD0; rho = 1 / sigma to 0x3F2B7672.  For d = p:
+    p * rho = 0x3F337FFF, just below the bf16 midpoint 0.701171875 =
+    0x3F338000, so n = 0x3F33 (0.69921875), which is also where the exact
+    p / sqrt(var + eps) = 0.70117182... lies.  Dividing instead, p / sigma
+    rounds to the midpoint itself and then to the even 0x3F34."""
+    x = np.array([0x3F86, 0xBF86, 0x3FF9, 0xBFF9, 0x3FD9, 0xBFD9, 0x3F8A, 0xBF8A], np.uint16)
+    xv = value_of_bf16(x)
+    assert list(xv[::2]) == [1.046875, 1.9453125, 1.6953125, 1.078125]
+    var = sum(Fraction(float(v)) ** 2 for v in xv) / 8
+    assert var == Fraction(2.229156494140625)
+    f = np.float32
+    sig = np.sqrt(f(2.229156494140625) + f(1e-6))
+    assert sig.view(np.uint32) == 0x3FBF1BD0
+    rho = f(1) / sig
+    assert rho.view(np.uint32) == 0x3F2B7672
+    assert (f(xv[0]) * rho).view(np.uint32) == 0x3F337FFF
+    assert (f(xv[0]) / sig).view(np.uint32) == 0x3F338000          # the other reading
+    n, (mu, v, r) = oracle.ln_row(x, 1e-6)
+    assert mu == 0 and v == np.float32(2.229156494140625) and r == rho
+    assert n[0] == 0x3F33 and n[1] == 0xBF33
+
+
 def _ln_double(xv, eps):
     mu = xv.mean()
     var = ((xv - mu) ** 2).mean()
@@ -423,6 +454,61 @@ def test_rms_rounded_squares_closed_form():
     _, (ms, v, rstd) = oracle.rms_row(x, w, 1e-6)
     assert ms == np.float32(1.078125 * 2.0 ** -18)
     assert v == np.float32(172 * 2.0 ** -25)
+
+
+def test_rms_y1_rounded_before_the_weight():
+    """y1 = bf(x * rstd) is rounded before the weight multiplies it (page
+    "#34085 [diffusion] Clean up kernels and shared fast paths", section
+    "关键源码片段": the normalized row is cast to bf16, then multiplied by the
+    weight).  The row of test_rms_rounded_squares_closed_form has rstd =
+    247/256.  For x = 137/128 (1.0703125): x * rstd = 33839/32768 =
+    132.18 steps of 2^-7, so y1 = 132/128.  With w = 255/128 (1.9921875):
+    y1 * w = 33660/16384 = 131.48 steps of 2^-6, so y2 = 131/64 (0x4003);
+    without the rounding of y1, 33839 * 255 / 2^22 = 131.67 steps gives
+    132/64 (0x4004).  For x = 1: x * rstd = 247/256 is exact and
+    y2 = bf(247 * 255 / 2^15) = 246/128 (0x3FF6) either way."""
+    D = 1024
+    x = np.empty(D, dtype=np.uint16)
+    x[0::2] = 0x3F80
+    x[1::2] = 0x3F89
+    w = np.full(D, 0x3FFF, dtype=np.uint16)
+    assert value_of_bf16(np.array([0x3FFF]))[0] == 255 / 128
+    y1 = Fraction(137, 128) * Fraction(247, 256)
+    assert frac_bf16(y1) == 0x3F84                                   # 132/128
+    assert frac_bf16(Fraction(132, 128) * Fraction(255, 128)) == 0x4003
+    assert frac_bf16(y1 * Fraction(255, 128)) == 0x4004              # the other reading
+    y2, (_, _, rstd) = oracle.rms_row(x, w, 1e-6)
+    assert rstd == np.float32(247 / 256)
+    assert np.all(y2[1::2] == 0x4003) and np.all(y2[0::2] == 0x3FF6)
+    scale = np.full((1, D), 0x3F80, dtype=np.uint16)
+    out = oracle.rmsnorm_scale(x[None], w, scale)
+    assert np.array_equal(out[0], y2)
+
+
+def test_rms_rstd_taken_from_the_rounded_mean_square_plus_eps():
+    """rstd is computed from v = bf(ms + eps), the bf16 value of the sum (page
+    "#34085 [diffusion] Clean up kernels and shared fast paths", section
+    "关键源码片段": the mean square plus eps is cast to bf16 before the rsqrt).
+    Constant row x = 2^-14, D = 1024, eps = 1e-6 (binary32 0x358637BD):
+    squares 2^-28 (exact), ms = 2^-28; ms + eps = 1.00372529e-6 (0x3586B7BD)
+    = 134.72 steps of 2^-27, so v = 135 * 2^-27 (bf16 0x3587).  1/sqrt(v) =
+    997.10 rounds to 996 (bf16 steps of 4 in [512, 1024)), and y1 =
+    996 * 2^-14 = 249 * 2^-12 (0x3D79).  Taken from the unrounded sum,
+    1/sqrt(1.00372529e-6) = 998.14 would round to 1000, y1 = 0x3D7A."""
+    D = 1024
+    x = np.full(D, 0x3880, dtype=np.uint16)
+    assert value_of_bf16(x[:1])[0] == 2.0 ** -14
+    w = np.full(D, 0x3F80, dtype=np.uint16)
+    f = np.float32
+    s = f(2.0 ** -28) + f(1e-6)
+    assert s.view(np.uint32) == 0x3586B7BD
+    assert frac_bf16(Fraction(float(s))) == 0x3587
+    v = Fraction(135, 2 ** 27)
+    assert frac_bf16(Fraction(float(f(1) / np.sqrt(f(float(v)))))) == 0x4479   # 996
+    assert frac_bf16(Fraction(float(f(1) / np.sqrt(s)))) == 0x447A             # 1000
+    y2, (ms, vv, rstd) = oracle.rms_row(x, w, 1e-6)
+    assert ms == np.float32(2.0 ** -28) and vv == np.float32(float(v)) and rstd == 996
+    assert np.all(y2 == 0x3D79)
 
 
 def test_rms_chain_near_ideal_and_unit_rms():
@@ -802,6 +888,65 @@ def test_qk_head_quarter_and_half_turns():
     assert np.array_equal(value_of_bf16(q[0::2]), -value_of_bf16(u[1::2]))
     assert np.array_equal(value_of_bf16(q[1::2]), value_of_bf16(u[0::2]))
     assert np.array_equal(value_of_bf16(h), -value_of_bf16(u))
+
+
+def test_qk_head_normalized_value_rounded_before_the_weight():
+    """The Q/K head norm rounds bf(x * rho) before the weight multiplies it
+    (page "基于Agent的SGLang扩散模型Kernel优化实践", section "合并QKV投影时的数值
+    问题": normalize, then apply the per-head-dim weight, each in bf16).
+    Hand-derived head, Dh = 128, eps = 1e-6: x = (1.0625, -1.0625, 0.75,
+    0.375, 0.1875, 0.0625, 2, then 121 ones), whose squares sum to 128
+    exactly, so ms = 1; ms + eps rounds to 1 + 2^-20, its square root to
+    1 + 2^-21 and rho = 1 / that to 1 - 2^-21 (0x3F7FFFF8).  x0 * rho =
+    1.0625 - 4 * 2^-23 (0x3F87FFFC) rounds to bf16 1.0625; with w0 = 1.1875
+    (0x3F98) the product 1.26171875 is exactly the midpoint between 161/128
+    and 162/128 and ties to the even 162/128 = 1.265625 (0x3FA2).  Without
+    the first rounding, (1.0625 - 4 * 2^-23) * 1.1875 lies below that
+    midpoint and gives 161/128 (0x3FA1).  cos = 1, sin = 0 leaves u as it is."""
+    vals = [1.0625, -1.0625, 0.75, 0.375, 0.1875, 0.0625, 2.0] + [1.0] * 121
+    assert sum(Fraction(v) ** 2 for v in vals) == 128
+    x = nearest_bf16(np.array(vals))
+    w = np.full(128, 0x3F80, dtype=np.uint16)
+    w[0] = 0x3F98
+    f = np.float32
+    rho = f(1) / np.sqrt(f(1) + f(1e-6))
+    assert Fraction(float(rho)) == 1 - Fraction(1, 2 ** 21)
+    n0 = f(1.0625) * rho
+    assert Fraction(float(n0)) == Fraction(1.0625) - Fraction(4, 2 ** 23)
+    assert frac_bf16(Fraction(float(n0))) == 0x3F88
+    assert frac_bf16(Fraction(1.0625) * Fraction(1.1875)) == 0x3FA2
+    assert frac_bf16(Fraction(float(n0 * f(1.1875)))) == 0x3FA1          # the other reading
+    o = oracle.qk_head(x, w, np.ones(64, np.float32), np.zeros(64, np.float32), 1e-6)
+    assert o[0] == 0x3FA2
+    assert np.array_equal(o[1:], x[1:])          # bf(x * rho) = x for the others, w = 1
+
+
+def test_qk_head_rope_products_rounded_separately():
+    """RoPE rounds each product to binary32 before the sum, with no fused
+    multiply-add (the lossless reading of the interleaved rotation on page
+    "基于Agent的SGLang扩散模型Kernel优化实践", section "合并QKV投影时的数值问题").
+    A constant head x = 1 has ms = 1, so bf(x * rho) = 1 and u = w.  With
+    u = (a, a, a, -a, 1, 1, ...) for a = 129/128 and a 45-degree rotation
+    (cos = sin = c = 0x3F3504F3): o0 = a*c - a*c and o3 = a*c + (-a)*c are
+    differences of two equal rounded products, exactly +0; o1 = o2 = 2 a*c
+    rounds to 0x3FB6.  A fused form would leave the rounding error of a*c,
+    a*c - fp32(a*c) = -6.05e-9 (bf16 0xB1D0), in o0 and o3."""
+    x = np.full(128, 0x3F80, dtype=np.uint16)
+    w = np.full(128, 0x3F80, dtype=np.uint16)
+    w[0] = w[1] = w[2] = 0x3F81
+    w[3] = 0xBF81
+    c = np.full(64, np.sqrt(0.5), dtype=np.float32)
+    assert c[0].view(np.uint32) == 0x3F3504F3
+    u = oracle.qk_head(x, w, np.ones(64, np.float32), np.zeros(64, np.float32), 1e-6)
+    assert np.array_equal(u, w)
+    a, cc = Fraction(129, 128), Fraction(float(c[0]))
+    ac = Fraction(float(np.float32(float(a * cc))))          # a*c is exact in float64
+    assert ac != a * cc
+    assert frac_bf16(a * cc - ac) == 0xB1D0                   # the fused form's o0
+    assert frac_bf16(2 * ac) == 0x3FB6
+    o = oracle.qk_head(x, w, c, c, 1e-6)
+    assert list(o[:4]) == [0x0000, 0x3FB6, 0x3FB6, 0x0000]
+    assert np.all(o[4::2] == 0x0000)                          # (1, 1): c - c
 
 
 def test_qk_head_rotation_preserves_norm_and_matches_double():
