@@ -6,7 +6,13 @@ the C entry point of the same name on the current torch stream.  Every step
 of the computation runs in the HIP kernels; there is no CPU or PyTorch
 fallback.  A problem outside the fast path raises ``DitUnsupported`` (the
 caller decides what to run instead); bad arguments raise ``DitInvalid``.
+
+The probes of the device primitives and the dispatch-timing hook live in
+libdit_probe.so, which links the same kernel objects; ``instrumented()``
+routes the epilogue calls made inside it through that library, so that
+``dit_time_next_launch`` can time them.
 """
+import contextlib
 import ctypes
 import os
 
@@ -14,6 +20,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdit.so")
+PROBE_LIB_PATH = os.path.join(_PKG, "libdit_probe.so")
 
 LOSSLESS = 0
 FAST = 1
@@ -48,8 +55,10 @@ class QkvStream(ctypes.Structure):
 
 
 _lib = None
+_probe_lib = None
+_route_probe = False
 
-# name -> argtypes of every exported function
+# name -> argtypes of every entry point of libdit.so
 SIGNATURES = {
     "dit_abi_version": [],
     "dit_status_string": [_int],
@@ -67,7 +76,6 @@ SIGNATURES = {
                             _f32, _vp, _int, _vp],
     "dit_gate_add_ln_modulate_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                      _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _int, _vp],
-    "dit_probe_fp8": [_int, _vp, _vp, _i64, _vp, _vp],
     "dit_wan_modulation_table": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp],
     "dit_qk_norm_rope": [_vp, _vp, _vp, _i64, _i64, ctypes.POINTER(QkvStream),
                          ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp],
@@ -76,6 +84,11 @@ SIGNATURES = {
     "dit_qk_norm_rope_dest": [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.POINTER(QkvStream),
                               ctypes.POINTER(QkvStream), _vp, _vp, _i64, _i64, _i64, _f32, _int,
                               _vp],
+}
+
+# the additional entry points of libdit_probe.so
+PROBE_SIGNATURES = {
+    "dit_probe_fp8": [_int, _vp, _vp, _i64, _vp, _vp],
     "dit_probe_bf16_round": [_vp, _vp, _i64, _vp],
     "dit_probe_unary": [_int, _vp, _vp, _i64, _int, _vp],
     "dit_probe_f32": [_int, _vp, _vp, _vp, _i64, _int, _vp],
@@ -85,29 +98,59 @@ SIGNATURES = {
 }
 
 
+def _load(path, signatures):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with "
+                           "`python -m modulation_bf16_row_amd.build`")
+    h = ctypes.CDLL(path)
+    for name, args in signatures.items():
+        fn = getattr(h, name)
+        fn.argtypes = args
+        fn.restype = _int
+    h.dit_status_string.restype = ctypes.c_char_p
+    h.dit_status_reason.restype = ctypes.c_char_p
+    return h
+
+
 def lib():
     """The loaded libdit.so.  Raises if it has not been built: there is no
     fallback implementation."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
-                               "`python -m modulation_bf16_row_amd.build`")
-        h = ctypes.CDLL(LIB_PATH)
-        for name, args in SIGNATURES.items():
-            fn = getattr(h, name)
-            fn.argtypes = args
-            fn.restype = _int
-        h.dit_status_string.restype = ctypes.c_char_p
-        h.dit_status_reason.restype = ctypes.c_char_p
-        _lib = h
+        _lib = _load(LIB_PATH, SIGNATURES)
     return _lib
 
 
-def _check(status):
+def probe_lib():
+    """The loaded libdit_probe.so (the product's kernels plus the probes and
+    the timing hook)."""
+    global _probe_lib
+    if _probe_lib is None:
+        _probe_lib = _load(PROBE_LIB_PATH, {**SIGNATURES, **PROBE_SIGNATURES})
+    return _probe_lib
+
+
+@contextlib.contextmanager
+def instrumented():
+    """Epilogue calls made (or prepared) inside go through libdit_probe.so:
+    the same kernel objects, launched so that a pending dit_time_next_launch
+    registration times them."""
+    global _route_probe
+    prev, _route_probe = _route_probe, True
+    try:
+        yield
+    finally:
+        _route_probe = prev
+
+
+def _epilogue_lib():
+    return probe_lib() if _route_probe else lib()
+
+
+def _check(status, h=None):
     if status == 0:
         return
-    reason = lib().dit_status_reason().decode()
+    reason = (h or lib()).dit_status_reason().decode()
     if status == 1:
         raise DitUnsupported(reason)
     if status == 2:
@@ -183,26 +226,27 @@ class PreparedCall:
     """A fully marshalled epilogue call: checks and argument conversion were
     done once, on the stream that was current then; calling it only enqueues
     the kernel (one C call).  Returns the output tensor(s)."""
-    __slots__ = ("_fn", "_args", "_result")
+    __slots__ = ("_fn", "_args", "_result", "_lib")
 
-    def __init__(self, fn, args, result):
-        self._fn, self._args, self._result = fn, args, result
+    def __init__(self, fn, args, result, h):
+        self._fn, self._args, self._result, self._lib = fn, args, result, h
 
     def __call__(self):
         status = self._fn(*self._args)
         if status:
-            _check(status)
+            _check(status, self._lib)
         return self._result
 
 
 def _call(name, result, prepare, *args):
-    fn = getattr(lib(), name)
+    h = _epilogue_lib()
+    fn = getattr(h, name)
     if prepare:
         conv = tuple(t(a) if not isinstance(a, (ctypes._SimpleCData, ctypes.Structure,
                                                  ctypes._Pointer)) and t is not None else a
                      for a, t in zip(args, SIGNATURES[name]))
-        return PreparedCall(fn, conv, result)
-    _check(fn(*args))
+        return PreparedCall(fn, conv, result, h)
+    _check(fn(*args), h)
     return result
 
 
@@ -488,34 +532,40 @@ def dit_qk_norm_rope_packed(txt, img, cos, sin, dests, eps=1e-6, mode="lossless"
 
 
 def dit_time_next_launch(start, stop):
-    """Makes the next epilogue call on this thread record `start` / `stop`
+    """Makes the next call on this thread into libdit_probe.so (an epilogue
+    inside ``instrumented()``, or a probe) record `start` / `stop`
     (torch.cuda.Event objects that have been recorded once, so that they
     exist) around its kernel, from within the dispatch."""
-    _check(lib().dit_time_next_launch(_vp(start.cuda_event), _vp(stop.cuda_event)))
+    h = probe_lib()
+    _check(h.dit_time_next_launch(_vp(start.cuda_event), _vp(stop.cuda_event)), h)
 
 
-# --- probes of the device primitives ---------------------------------------------------
+# --- probes of the device primitives (libdit_probe.so) ---------------------------------
+
+def _pcheck(status):
+    _check(status, probe_lib())
+
 
 def dit_probe_bf16_round(x_f32, out=None):
     if out is None:
         out = torch.empty(x_f32.shape, dtype=torch.int16, device=x_f32.device)
-    _check(lib().dit_probe_bf16_round(out.data_ptr(), x_f32.data_ptr(), x_f32.numel(),
-                                      _stream(x_f32)))
+    _pcheck(probe_lib().dit_probe_bf16_round(out.data_ptr(), x_f32.data_ptr(), x_f32.numel(),
+                                             _stream(x_f32)))
     return out
 
 
 def dit_probe_unary(op, h_i16, mode="lossless"):
     out = torch.empty_like(h_i16)
-    _check(lib().dit_probe_unary(op, out.data_ptr(), h_i16.data_ptr(), h_i16.numel(),
-                                 _mode(mode), _stream(h_i16)))
+    _pcheck(probe_lib().dit_probe_unary(op, out.data_ptr(), h_i16.data_ptr(), h_i16.numel(),
+                                        _mode(mode), _stream(h_i16)))
     return out
 
 
 def dit_probe_f32(op, a, b=None, mode="lossless"):
     out = torch.empty_like(a)
-    _check(lib().dit_probe_f32(op, out.data_ptr(), a.data_ptr(),
-                               b.data_ptr() if b is not None else None, a.numel(), _mode(mode),
-                               _stream(a)))
+    _pcheck(probe_lib().dit_probe_f32(op, out.data_ptr(), a.data_ptr(),
+                                      b.data_ptr() if b is not None else None, a.numel(), _mode(mode),
+                                      _stream(a)))
     return out
 
 
@@ -524,7 +574,7 @@ def dit_probe_copy(dst, src, flags=0):
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise DitInvalid("dst and src sizes differ")
-    _check(lib().dit_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, flags, _stream(src)))
+    _pcheck(probe_lib().dit_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, flags, _stream(src)))
     return dst
 
 
@@ -532,8 +582,8 @@ def dit_probe_fp8(op, inp, scale=None):
     """op 0: E4M3 codes of a float32 tensor; op 1: E4M3 codes of a bfloat16
     tensor divided by scale (one-element float32 tensor).  Returns uint8."""
     out = torch.empty(inp.shape, dtype=torch.uint8, device=inp.device)
-    _check(lib().dit_probe_fp8(op, out.data_ptr(), inp.data_ptr(), inp.numel(),
-                               scale.data_ptr() if scale is not None else None, _stream(inp)))
+    _pcheck(probe_lib().dit_probe_fp8(op, out.data_ptr(), inp.data_ptr(), inp.numel(),
+                                      scale.data_ptr() if scale is not None else None, _stream(inp)))
     return out
 
 
@@ -541,6 +591,6 @@ def dit_probe_row_sum(t, head=False):
     """t: float32 [rows, dim] contiguous -> float32 [rows] (head: [groups])."""
     rows, dim = t.shape
     out = torch.empty(rows, dtype=torch.float32, device=t.device)
-    _check(lib().dit_probe_row_sum(out.data_ptr(), t.data_ptr(), rows, dim, int(head),
-                                   _stream(t)))
+    _pcheck(probe_lib().dit_probe_row_sum(out.data_ptr(), t.data_ptr(), rows, dim, int(head),
+                                          _stream(t)))
     return out

@@ -1,7 +1,18 @@
-"""Builds the HIP epilogue library, modulation_bf16_row_amd/libdit.so, for gfx950.
+"""Builds the HIP epilogue library for gfx950.
 
 Every source is compiled with hipcc for gfx950 only, in parallel, into
-_build/, then linked into one shared library with a plain C ABI.
+_build/, then linked twice from the same objects:
+
+  libdit.so        the product: the entry points of include/dit.h and
+                   include/dit_producers.h, nothing else exported;
+  libdit_probe.so  the same kernel and guard objects plus the probes of the
+                   device primitives (include/dit_probe.h) and the
+                   dispatch-timing hook (include/dit_timing.h), for the tests
+                   and the benchmark's per-kernel timing.
+
+A linker version script limits each library's dynamic symbols to the
+declared entry points (and the compiler's per-translation-unit
+__hip_cuid_* markers).
 
 Floating-point flags: no contraction into fused multiply-add
 (-ffp-contract=off; FAST-mode code writes fmaf explicitly), no fast-math,
@@ -11,6 +22,7 @@ harmless warning that it does not know this feature).
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -20,9 +32,17 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdit.so")
+PROBE_LIB = os.path.join(PKG, "libdit_probe.so")
 
-SOURCES = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_mod.hip",
-           "dit_qkv.hip", "dit_modtab.hip", "dit_probe.hip", "dit_abi.cpp"]
+# Kernels and the C-ABI guards, shared by both libraries.
+KERNELS = ["dit_ln.hip", "dit_gate_ln.hip", "dit_rms.hip", "dit_gate.hip", "dit_mod.hip",
+           "dit_qkv.hip", "dit_modtab.hip", "dit_abi.cpp"]
+PRODUCT_ONLY = ["dit_timing_off.cpp"]
+PROBE_ONLY = ["dit_probe.hip", "dit_probe_abi.cpp"]
+SOURCES = KERNELS + PRODUCT_ONLY + PROBE_ONLY
+
+PRODUCT_HEADERS = ["dit.h", "dit_producers.h"]
+PROBE_HEADERS = PRODUCT_HEADERS + ["dit_probe.h", "dit_timing.h"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -60,21 +80,40 @@ def _compile(src, verbose, build_dir, extra):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 7, lib: str = LIB, extra_flags=()) -> str:
-    """Compiles and links the library; `lib` and `extra_flags` allow side
-    builds (e.g. with -D macros) without touching the default one."""
-    build_dir = BUILD if lib == LIB else os.path.join(BUILD, os.path.basename(lib) + ".d")
-    os.makedirs(build_dir, exist_ok=True)
-    extra = list(extra_flags)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
-    tmp = lib + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+def declared_entry_points(headers):
+    """Names of the functions the given include/ headers declare."""
+    names = set()
+    for h in headers:
+        text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dit_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def _link(objs, headers, out, build_dir, verbose):
+    script = os.path.join(build_dir, os.path.basename(out) + ".map")
+    with open(script, "w") as f:
+        f.write("{\n  global:\n")
+        for n in declared_entry_points(headers):
+            f.write(f"    {n};\n")
+        f.write("    __hip_cuid_*;\n")          # the compiler's per-TU ids stay as they were
+        f.write("  local:\n    *;\n};\n")
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+           f"-Wl,--version-script={script}", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, lib)
-    return lib
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 7) -> str:
+    """Compiles every source and links libdit.so and libdit_probe.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(SOURCES, ex.map(lambda s: _compile(s, verbose, BUILD, []), SOURCES)))
+    _link([objs[s] for s in KERNELS + PRODUCT_ONLY], PRODUCT_HEADERS, LIB, BUILD, verbose)
+    _link([objs[s] for s in KERNELS + PROBE_ONLY], PROBE_HEADERS, PROBE_LIB, BUILD, verbose)
+    return LIB
 
 
 if __name__ == "__main__":

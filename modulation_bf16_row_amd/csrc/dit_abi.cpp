@@ -14,66 +14,87 @@
 #include <algorithm>
 
 #include "dit.h"
+#include "dit_guard.hpp"
 #include "dit_launch.hpp"
-#include "dit_probe.h"
 #include "dit_producers.h"
-#include "dit_timing.h"
+
+namespace dit {
+namespace guard {
 
 namespace {
-
 thread_local const char *g_reason = "";
-thread_local hipEvent_t g_time_start = nullptr;
-thread_local hipEvent_t g_time_stop = nullptr;
+
+using i128 = __int128;
+
+i128 floor_div(i128 a, i128 b) {  // b > 0
+  i128 q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+}  // namespace
 
 dit_status_t fail(dit_status_t s, const char *why) {
   g_reason = why;
   return s;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+const char *reason() { return g_reason; }
 
-// A set of byte segments [base + i*step, base + i*step + len), i < count.
-struct Span {
-  uintptr_t base;
-  int64_t step;
-  int64_t count;
-  int64_t len;
-};
-
-int64_t floor_div(int64_t a, int64_t b) {  // b > 0
-  int64_t q = a / b;
-  return (a % b != 0 && a < 0) ? q - 1 : q;
+dit_status_t hip_status(hipError_t e) {
+  if (e != hipSuccess) return fail(DIT_ERR_HIP, hipGetErrorString(e));
+  return DIT_OK;
 }
 
-// True if some byte belongs to both spans.  Exact when both have the same
-// step (or one has a single segment); otherwise compares the hulls, which
-// may report an overlap that the segments avoid (the safe direction).
+bool extent_ok(const void *p, int64_t step, int64_t count, int64_t len, int64_t esz) {
+  if (count <= 0 || len <= 0) return true;
+  const i128 bytes = ((i128)(count - 1) * step + len) * esz;
+  if (bytes > kMaxExtentBytes) return false;
+  const unsigned __int128 end = (unsigned __int128)reinterpret_cast<uintptr_t>(p) + bytes;
+  return end <= ((unsigned __int128)1 << 64);
+}
+
 bool spans_overlap(Span a, Span b) {
   if (a.count <= 0 || b.count <= 0 || a.len <= 0 || b.len <= 0) return false;
   if (a.count == 1 || a.step <= 0) { a.count = 1; a.step = b.step; }
   if (b.count == 1 || b.step <= 0) { b.count = 1; b.step = a.step; }
-  const uintptr_t a_end = a.base + (uintptr_t)((a.count - 1) * a.step + a.len);
-  const uintptr_t b_end = b.base + (uintptr_t)((b.count - 1) * b.step + b.len);
-  if (a_end <= b.base || b_end <= a.base) return false;
+  const i128 a0 = (i128)a.base, b0 = (i128)b.base;
+  const i128 a_end = a0 + (i128)(a.count - 1) * a.step + a.len;
+  const i128 b_end = b0 + (i128)(b.count - 1) * b.step + b.len;
+  if (a_end <= b0 || b_end <= a0) return false;
   if (a.step != b.step || a.step <= 0) return true;
   // overlap iff -a.len < delta + m*step < b.len for some m in
   // [-(a.count-1), b.count-1], delta = b.base - a.base
-  const int64_t delta = (int64_t)(b.base - a.base);
-  int64_t m = floor_div(-a.len - delta, a.step) + 1;
-  m = std::max(m, -(a.count - 1));
-  if (m > b.count - 1) return false;
+  const i128 delta = b0 - a0;
+  i128 m = floor_div(-(i128)a.len - delta, a.step) + 1;
+  m = std::max(m, -(i128)(a.count - 1));
+  if (m > (i128)(b.count - 1)) return false;
   return delta + m * a.step < b.len;
 }
 
+}  // namespace guard
+}  // namespace dit
+
+namespace {
+
+using dit::guard::aligned16;
+using dit::guard::fail;
+using dit::guard::hip_status;
+using dit::guard::Span;
+using dit::guard::spans_overlap;
+
+// Byte segments of a flat row tensor (element stride 1, bf16).  The row
+// stride only matters when there is more than one row.
 Span rows_span(const void *p, int64_t rs, int64_t rows, int64_t dim) {
-  return Span{reinterpret_cast<uintptr_t>(p), rs * 2, rows, dim * 2};
+  return Span{reinterpret_cast<uintptr_t>(p), rows > 1 ? rs * 2 : 0, rows, dim * 2};
 }
 
 // Common checks of a row tensor argument; returns DIT_OK or the failure.
+// The extent check comes before any other arithmetic on the stride.
 dit_status_t check_rows(const void *p, int64_t rs, int64_t rows, int64_t dim, const char *null_msg,
                         const char *stride_msg) {
   if (!p) return fail(DIT_ERR_INVALID, null_msg);
   if (rs < 0) return fail(DIT_ERR_INVALID, stride_msg);
+  if (!dit::guard::extent_ok(p, rs, rows, dim, 2))
+    return fail(DIT_ERR_INVALID, "tensor extent exceeds 2^56 bytes or the address space");
   if (rows > 1 && (rs < dim || rs % 8 != 0)) return fail(DIT_ERR_UNSUPPORTED, stride_msg);
   if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "tensor pointer is not 16-byte aligned");
   return DIT_OK;
@@ -86,6 +107,10 @@ struct RowProblem {
   int mode;
 };
 
+// Row counts up to 4 (2^31 - 1): the row kernels' grids hold at most 2^31 - 1
+// workgroups of four rows.
+constexpr int64_t kMaxRows = int64_t(4) * 0x7FFFFFFF;
+
 dit_status_t check_shape(const RowProblem &p, bool has_mode) {
   if (has_mode && p.mode != DIT_MODE_LOSSLESS && p.mode != DIT_MODE_FAST)
     return fail(DIT_ERR_INVALID, "unknown mode");
@@ -97,7 +122,7 @@ dit_status_t check_shape(const RowProblem &p, bool has_mode) {
   if (p.dim % 8 != 0) return fail(DIT_ERR_UNSUPPORTED, "dim % 8 != 0");
   if (p.mod_rows == 0) return fail(DIT_ERR_INVALID, "mod_rows == 0 with rows > 0");
   if (p.rows % p.mod_rows != 0) return fail(DIT_ERR_UNSUPPORTED, "rows % mod_rows != 0");
-  if ((p.rows + 3) / 4 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
+  if (p.rows > kMaxRows) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
   return DIT_OK;
 }
 
@@ -114,11 +139,6 @@ dit_status_t check_out_alias(const Span &out, const Span *ins, int n_ins, const 
   return DIT_OK;
 }
 
-dit_status_t hip_status(hipError_t e) {
-  if (e != hipSuccess) return fail(DIT_ERR_HIP, hipGetErrorString(e));
-  return DIT_OK;
-}
-
 #define DIT_TRY(expr)                    \
   do {                                   \
     dit_status_t _s = (expr);            \
@@ -129,23 +149,9 @@ const uint16_t *u16(const void *p) { return static_cast<const uint16_t *>(p); }
 
 }  // namespace
 
-bool dit::take_timing_events(hipEvent_t *start, hipEvent_t *stop) {
-  if (!g_time_start && !g_time_stop) return false;
-  *start = g_time_start;
-  *stop = g_time_stop;
-  g_time_start = g_time_stop = nullptr;
-  return true;
-}
-
 extern "C" {
 
 int dit_abi_version(void) { return DIT_ABI_VERSION; }
-
-dit_status_t dit_time_next_launch(hipEvent_t start, hipEvent_t stop) {
-  g_time_start = start;
-  g_time_stop = stop;
-  return DIT_OK;
-}
 
 const char *dit_status_string(dit_status_t s) {
   switch (s) {
@@ -157,7 +163,7 @@ const char *dit_status_string(dit_status_t s) {
   return "DIT_STATUS_UNKNOWN";
 }
 
-const char *dit_status_reason(void) { return g_reason; }
+const char *dit_status_reason(void) { return dit::guard::reason(); }
 
 dit_status_t dit_ln_modulate(void *out, int64_t out_rs, const void *x, int64_t x_rs,
                              const void *scale, const void *shift, int64_t mod_rs,
@@ -307,13 +313,15 @@ dit_status_t check_fp8(void *out8, int64_t out8_rs, const float *fp8_scale, int6
   if (!out8) return fail(DIT_ERR_INVALID, "out_fp8 is NULL");
   if (!fp8_scale) return fail(DIT_ERR_INVALID, "fp8_scale is NULL");
   if (out8_rs < 0) return fail(DIT_ERR_INVALID, "bad out_fp8 row stride");
+  if (!dit::guard::extent_ok(out8, out8_rs, rows, dim, 1))
+    return fail(DIT_ERR_INVALID, "out_fp8 extent exceeds 2^56 bytes or the address space");
   if (rows > 1 && (out8_rs < dim || out8_rs % 8 != 0))
     return fail(DIT_ERR_UNSUPPORTED, "bad out_fp8 row stride");
   if ((reinterpret_cast<uintptr_t>(out8) & 7u) != 0)
     return fail(DIT_ERR_UNSUPPORTED, "out_fp8 is not 8-byte aligned");
   if ((reinterpret_cast<uintptr_t>(fp8_scale) & 3u) != 0)
     return fail(DIT_ERR_UNSUPPORTED, "fp8_scale is not 4-byte aligned");
-  const Span s8{reinterpret_cast<uintptr_t>(out8), out8_rs, rows, dim};
+  const Span s8{reinterpret_cast<uintptr_t>(out8), rows > 1 ? out8_rs : 0, rows, dim};
   const Span sc{reinterpret_cast<uintptr_t>(fp8_scale), 0, 1, 4};
   if (spans_overlap(s8, sc)) return fail(DIT_ERR_INVALID, "out_fp8 overlaps fp8_scale");
   for (int i = 0; i < n_others; ++i) {
@@ -340,7 +348,10 @@ dit_status_t dit_wan_modulation_table(float *out, const float *table, const void
   if (n_mod > 64) return fail(DIT_ERR_UNSUPPORTED, "n_mod > 64");
   if (batch > (int64_t(1) << 32) / tokens || dim > 65536)
     return fail(DIT_ERR_UNSUPPORTED, "problem too large");
-  const int64_t n = n_mod * batch * tokens * dim;
+  const int64_t n = n_mod * batch * tokens * dim;   // <= 2^54: bounded above
+  if (!dit::guard::extent_ok(out, 0, 1, n, 4) || !dit::guard::extent_ok(temb, 0, 1, n, 2) ||
+      !dit::guard::extent_ok(table, 0, 1, n_mod * dim, 4))
+    return fail(DIT_ERR_INVALID, "tensor extent exceeds 2^56 bytes or the address space");
   const Span so{reinterpret_cast<uintptr_t>(out), 0, 1, n * 4};
   const Span st{reinterpret_cast<uintptr_t>(table), 0, 1, n_mod * dim * 4};
   const Span se{reinterpret_cast<uintptr_t>(temb), 0, 1, n * 2};
@@ -447,6 +458,17 @@ Span lattice_span(const void *p, const Lattice &l, int64_t width) {
   return Span{base, inner * 2, last / inner + 1, width * 2};
 }
 
+// True when the view (elements of `esz` bytes) spans at most
+// kMaxExtentBytes and stays inside the address space.  Checked before any
+// other arithmetic on its strides.
+bool lattice_extent_ok(const void *p, const Lattice &l, int64_t width, int64_t esz) {
+  __int128 last = 0;
+  for (int i = 0; i < 3; ++i)
+    if (l.count[i] > 1) last += (__int128)(l.count[i] - 1) * l.stride[i];
+  if (last > dit::guard::kMaxExtentBytes) return false;
+  return dit::guard::extent_ok(p, (int64_t)last, 2, width, esz);
+}
+
 // True when the view's segments are pairwise disjoint because its levels
 // nest: in increasing stride order each stride is at least the extent of
 // everything inside it.  (A sufficient test; layouts whose levels
@@ -478,6 +500,8 @@ dit_status_t check_stream(const dit_qkv_stream_t *st, int64_t batch, int64_t wid
     return fail(DIT_ERR_INVALID, "stream pointer is NULL");
   if (st->tok_stride < 0 || st->batch_stride < 0)
     return fail(DIT_ERR_INVALID, "negative stream stride");
+  if (batch > 0x7FFFFFFF || st->tokens > (int64_t(1) << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
   if ((st->tokens > 1 && st->tok_stride < width) || st->tok_stride % 8 != 0)
     return fail(DIT_ERR_UNSUPPORTED, "stream token stride");
   if (batch > 1 && (st->batch_stride % 8 != 0 || st->batch_stride < width))
@@ -485,6 +509,10 @@ dit_status_t check_stream(const dit_qkv_stream_t *st, int64_t batch, int64_t wid
   const void *ps[] = {st->q, st->k, st->v, st->q_weight, st->k_weight};
   for (const void *p : ps)
     if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "stream pointer is not 16-byte aligned");
+  const Lattice l{{st->tok_stride, st->batch_stride, 0}, {st->tokens, batch, 1}};
+  for (const void *p : {st->q, st->k, st->v})
+    if (!lattice_extent_ok(p, l, width, 2))
+      return fail(DIT_ERR_INVALID, "stream extent exceeds 2^56 bytes or the address space");
   return DIT_OK;
 }
 
@@ -501,7 +529,9 @@ dit_status_t qkv_impl(void *q_out, void *k_out, void *v_out, int64_t out_tok_str
   const dit_qkv_stream_t *st_img = img ? img : &empty;
   if (st_txt->tokens < 0 || st_img->tokens < 0)
     return fail(DIT_ERR_INVALID, "negative token count");
-  const int64_t s_total = st_txt->tokens + st_img->tokens;
+  int64_t s_total;
+  if (__builtin_add_overflow(st_txt->tokens, st_img->tokens, &s_total))
+    return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
   if (batch == 0 || heads == 0 || s_total == 0) return DIT_OK;
   if (head_dim != DIT_QK_HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "head_dim != 128");
   if (heads > 64) return fail(DIT_ERR_UNSUPPORTED, "heads > 64");
@@ -522,12 +552,18 @@ dit_status_t qkv_impl(void *q_out, void *k_out, void *v_out, int64_t out_tok_str
   if (out_tok_stride % 8 != 0 || out_batch_stride % 8 != 0)
     return fail(DIT_ERR_UNSUPPORTED, "output strides");
   const Lattice lo{{out_tok_stride, out_batch_stride, dest_stride}, {s_total, batch, dests}};
+  for (const void *p : {q_out, k_out, v_out})
+    if (!lattice_extent_ok(p, lo, dwidth, 2))
+      return fail(DIT_ERR_INVALID, "output extent exceeds 2^56 bytes or the address space");
   if (!lattice_disjoint(lo, dwidth))
     return fail(DIT_ERR_UNSUPPORTED, "output strides make an output overlap itself");
   const void *ps[] = {q_out, k_out, v_out, cos, sin};
   for (const void *p : ps)
     if (!aligned16(p)) return fail(DIT_ERR_UNSUPPORTED, "pointer is not 16-byte aligned");
-  if ((batch * s_total + 3) / 4 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
+  if ((__int128)batch * s_total > kMaxRows) return fail(DIT_ERR_UNSUPPORTED, "too many tokens");
+  if (!dit::guard::extent_ok(cos, 0, 1, s_total * (head_dim / 2), 4) ||
+      !dit::guard::extent_ok(sin, 0, 1, s_total * (head_dim / 2), 4))
+    return fail(DIT_ERR_INVALID, "table extent exceeds the address space");
 
   const Span outs[3] = {lattice_span(q_out, lo, dwidth), lattice_span(k_out, lo, dwidth),
                         lattice_span(v_out, lo, dwidth)};
@@ -603,83 +639,3 @@ extern "C" dit_status_t dit_qk_norm_rope_dest(void *q_out, void *k_out, void *v_
   return qkv_impl(q_out, k_out, v_out, out_tok_stride, out_batch_stride, heads_per_dest,
                   dest_stride, txt, img, cos, sin, batch, heads, head_dim, eps, mode, stream);
 }
-
-// ---------------------------------------------------------------------------
-// Probes
-// ---------------------------------------------------------------------------
-extern "C" {
-
-dit_status_t dit_probe_bf16_round(uint16_t *out, const float *in, int64_t n, hipStream_t stream) {
-  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (n == 0) return DIT_OK;
-  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
-  return hip_status(dit::launch_probe_bf16_round(out, in, n, stream));
-}
-
-dit_status_t dit_probe_unary(int op, uint16_t *out, const uint16_t *in, int64_t n, int mode,
-                             hipStream_t stream) {
-  if (op != DIT_PROBE_ONE_PLUS && op != DIT_PROBE_RMS_RSTD && op != DIT_PROBE_TANH_TABLE)
-    return fail(DIT_ERR_INVALID, "bad op");
-  if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
-    return fail(DIT_ERR_INVALID, "unknown mode");
-  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (n == 0) return DIT_OK;
-  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
-  return hip_status(dit::launch_probe_unary(op, out, in, n, mode, stream));
-}
-
-dit_status_t dit_probe_f32(int op, float *out, const float *a, const float *b, int64_t n, int mode,
-                           hipStream_t stream) {
-  if (op < DIT_PROBE_DIV || op > DIT_PROBE_RSQRT) return fail(DIT_ERR_INVALID, "bad op");
-  if (mode != DIT_MODE_LOSSLESS && mode != DIT_MODE_FAST)
-    return fail(DIT_ERR_INVALID, "unknown mode");
-  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (n == 0) return DIT_OK;
-  if (!out || !a || (op == DIT_PROBE_DIV && !b)) return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
-  return hip_status(dit::launch_probe_f32(op, out, a, b, n, mode, stream));
-}
-
-dit_status_t dit_probe_fp8(int op, uint8_t *out, const void *in, int64_t n, const float *scale,
-                           hipStream_t stream) {
-  if (op != DIT_PROBE_E4M3 && op != DIT_PROBE_FP8_QUANT) return fail(DIT_ERR_INVALID, "bad op");
-  if (n < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (n == 0) return DIT_OK;
-  if (!out || !in || (op == DIT_PROBE_FP8_QUANT && !scale))
-    return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (n / 256 > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many elements");
-  return hip_status(dit::launch_probe_fp8(op, out, in, n, scale, stream));
-}
-
-dit_status_t dit_probe_copy(void *out, const void *in, int64_t bytes, int flags,
-                            hipStream_t stream) {
-  if (bytes < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (flags < 0 || flags > 7) return fail(DIT_ERR_INVALID, "flags must be in [0, 7]");
-  if (bytes == 0) return DIT_OK;
-  if (!out || !in) return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (bytes % 16 != 0 || !aligned16(out) || !aligned16(in))
-    return fail(DIT_ERR_UNSUPPORTED, "bytes and pointers must be multiples of 16");
-  if ((flags & 4) && bytes / 16 / 64 >= 0x7FFFFFFF)
-    return fail(DIT_ERR_UNSUPPORTED, "too many vectors for the one-shot layout");
-  if (spans_overlap(Span{reinterpret_cast<uintptr_t>(out), 0, 1, bytes},
-                    Span{reinterpret_cast<uintptr_t>(in), 0, 1, bytes}))
-    return fail(DIT_ERR_INVALID, "buffers overlap");
-  return hip_status(dit::launch_probe_copy(out, in, bytes / 16, flags, stream));
-}
-
-dit_status_t dit_probe_row_sum(float *out, const float *t, int64_t rows, int64_t dim, int head,
-                               hipStream_t stream) {
-  if (rows < 0 || dim < 0) return fail(DIT_ERR_INVALID, "negative size");
-  if (head != 0 && head != 1) return fail(DIT_ERR_INVALID, "head must be 0 or 1");
-  if (rows == 0) return DIT_OK;
-  if (!out || !t) return fail(DIT_ERR_INVALID, "NULL pointer");
-  if (head == 0 && (dim == 0 || dim > DIT_MAX_DIM || dim % 8 != 0))
-    return fail(DIT_ERR_UNSUPPORTED, "dim must be a multiple of 8 in [8, 8192]");
-  if (head == 1 && dim != DIT_QK_HEAD_DIM) return fail(DIT_ERR_UNSUPPORTED, "dim must be 128");
-  if (rows > 0x7FFFFFFF) return fail(DIT_ERR_UNSUPPORTED, "too many rows");
-  return hip_status(dit::launch_probe_row_sum(out, t, rows, dim, head, stream));
-}
-
-}  // extern "C"

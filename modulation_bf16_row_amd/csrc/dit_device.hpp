@@ -175,8 +175,7 @@ struct V8 {
 // outputs) are touched once per call, so they are moved with nontemporal
 // loads and stores, which measured 9% faster on a pure copy than the default
 // policy.  Operands shared by many rows (weights, per-batch modulation rows,
-// cos/sin) use the default policy so they stay cached.  DIT_NO_NT_LOAD /
-// DIT_NO_NT_STORE restore the default policy (build-time experiments).
+// cos/sin) use the default policy so they stay cached.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ V8 load8(const uint16_t *p) {
@@ -185,21 +184,13 @@ __device__ __forceinline__ V8 load8(const uint16_t *p) {
 }
 
 __device__ __forceinline__ V8 load8_stream(const uint16_t *p) {
-#ifdef DIT_NO_NT_LOAD
-  return load8(p);
-#else
   const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return V8{{u[0], u[1], u[2], u[3]}};
-#endif
 }
 
 __device__ __forceinline__ void store8(uint16_t *p, const V8 &v) {
-#ifdef DIT_NO_NT_STORE
-  *reinterpret_cast<uint4 *>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-#else
   const u32x4 u = {v.w[0], v.w[1], v.w[2], v.w[3]};
   __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(p));
-#endif
 }
 
 // Eight bytes (two words) with a nontemporal store.

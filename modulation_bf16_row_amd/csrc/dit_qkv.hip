@@ -19,8 +19,6 @@
 // writes the destination-major buffer whose P contiguous chunks an
 // all-to-all hands one to each rank under Ulysses sequence parallelism (page
 // "基于Agent的SGLang扩散模型Kernel优化实践", section "Ulysses QKV仅执行一次All-to-All").
-#include <stdlib.h>
-
 #include "dit_device.hpp"
 #include "dit_launch.hpp"
 
@@ -149,8 +147,6 @@ __global__ __launch_bounds__(64 * kQkvWaves) __attribute__((amdgpu_waves_per_eu(
 // ceil(heads / 4) groups split into as few equal parts as that allows.  At
 // the Qwen-Image shape (24 heads) one group per wave (70 VGPRs, 7 waves per
 // SIMD) measured 57.3 us against 58.4, 59.8 and 64.4 us for 2, 3 and 6.
-// Only HG = 1 is built into the library; the tuning build instantiates up to
-// 16 groups per wave for such sweeps.
 constexpr int64_t kQkvTargetWaves = int64_t(1) << 20;
 constexpr int kQkvGroups = 1;
 
@@ -159,11 +155,7 @@ static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {
   const int64_t total = a.batch * a.s_total;
   a.tokens_per_wave = (total + kQkvTargetWaves - 1) / kQkvTargetWaves;
   const int groups = (int)((a.heads + 3) / 4);
-  int max_hg = kQkvGroups;
-#ifdef DIT_TUNING
-  if (const char *e = getenv("DIT_TOKENS_PER_WAVE")) a.tokens_per_wave = atoll(e);
-  if (const char *e = getenv("DIT_QKV_GROUPS")) max_hg = atoi(e);
-#endif
+  const int max_hg = kQkvGroups;
   a.parts = (groups + max_hg - 1) / max_hg;
   const int hg = (groups + (int)a.parts - 1) / (int)a.parts;
   const int64_t waves = (total + a.tokens_per_wave - 1) / a.tokens_per_wave * a.parts;
@@ -172,9 +164,6 @@ static hipError_t qkv_dispatch(QkvArgs a, hipStream_t s) {
 #define X(N) \
   case N: DIT_LAUNCH((k_qk_norm_rope<N, MODE>), grid, dim3(64 * kQkvWaves), 0, s, a); break;
     X(1)
-#ifdef DIT_TUNING
-    X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
-#endif
 #undef X
     default: return hipErrorInvalidValue;
   }

@@ -36,8 +36,6 @@
 // 一等公民", section 0x3 / 3.2.
 #pragma once
 
-#include <stdlib.h>
-
 #include "dit_device.hpp"
 #include "dit_launch.hpp"
 
@@ -56,11 +54,7 @@ static_assert(kThreads >= kTanhTabVecs, "one workgroup copies the tanh table in 
 // which it does not slow.  The same split in the standalone gate-add and
 // tanh-residual made those faster back to back but slowed LN and RMS-scale in
 // the five-kernel step by ~4 us each, so they keep both streams nontemporal.
-#ifdef DIT_NO_NT_LOAD
-constexpr bool kNtLn = false, kNtRms = false, kNtTanh = false, kNtGate = false, kNtMod = false;
-#else
 constexpr bool kNtLn = false, kNtRms = false, kNtTanh = true, kNtGate = true, kNtMod = false;
-#endif
 constexpr bool kNtGateLnY = false;
 
 // Register budget: at least W6 waves per SIMD at dim <= 3072 (NC <= 6),
@@ -241,16 +235,9 @@ inline size_t stage_bytes(int64_t dim, int rows) {
 inline Shape row_shape(int64_t rows, int64_t per_mod, int64_t dim, int staged_rows) {
   Shape s;
   s.rows_per_wave = 1;
-#ifdef DIT_TUNING
-  if (const char *e = getenv("DIT_ROWS_PER_WAVE")) s.rows_per_wave = atoll(e);
-#endif
-  if (s.rows_per_wave < 1) s.rows_per_wave = 1;
   const int64_t wg_rows = kWavesPerBlock * s.rows_per_wave;
   s.staged = staged_rows > 0 && per_mod >= wg_rows &&
              stage_bytes(dim, staged_rows) <= kMaxStagedLds;
-#ifdef DIT_TUNING
-  if (getenv("DIT_NO_STAGING")) s.staged = false;
-#endif
   const int64_t blocks_per_mod = (per_mod + wg_rows - 1) / wg_rows;
   if (s.staged && rows / per_mod * blocks_per_mod > 0x7FFFFFFF) s.staged = false;
   if (s.staged) {

@@ -14,3 +14,17 @@ if HERE not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long CPU sweep")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _sanitized_oracle():
+    """Under the sanitizer run (see tests/sanitizers.py) every oracle call
+    goes to the sanitized build of the oracle."""
+    import sanitizers
+    d = sanitizers.sanitized_dir()
+    if d is None:
+        yield
+        return
+    import oracle
+    with oracle.using_library(os.path.join(d, "liboracle.so")):
+        yield

@@ -12,6 +12,8 @@ import subprocess
 
 import pytest
 
+import sanitizers
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(ROOT, "modulation_bf16_row_amd", "csrc")
@@ -21,38 +23,61 @@ OK, UNSUPPORTED, INVALID, HIP = 0, 1, 2, 3
 vp, i64, f32, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
 
 
-def declared_functions():
+PROBE_LIB = os.path.join(ROOT, "modulation_bf16_row_amd", "libdit_probe.so")
+PRODUCT_HEADERS = ("dit.h", "dit_producers.h")
+PROBE_HEADERS = ("dit_probe.h", "dit_timing.h")
+
+
+def declared_functions(headers=None):
     names = set()
     for fn in os.listdir(INCLUDE):
-        if fn.endswith(".h"):
+        if fn.endswith(".h") and (headers is None or fn in headers):
             text = open(os.path.join(INCLUDE, fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
             names |= set(re.findall(r"\b(dit_\w+)\s*\(", text))
     return sorted(names)
 
 
-def test_library_exports_every_declared_function():
+def exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return sorted(l.split()[-1] for l in out.splitlines()
+                  if l.strip() and not l.split()[-1].startswith("__hip_cuid_"))
+
+
+def test_product_library_exports_exactly_the_product_headers():
+    """libdit.so exports the entry points of dit.h and dit_producers.h and
+    nothing else (no probes, no timing hook, no C++ internals)."""
     if not os.path.exists(LIB):
         pytest.skip("libdit.so not built")
+    names = declared_functions(PRODUCT_HEADERS)
+    assert len(names) >= 14
+    assert exported(LIB) == names
     lib = ctypes.CDLL(LIB)
-    names = declared_functions()
-    assert len(names) >= 12
-    missing = [n for n in names if not hasattr(lib, n)]
-    assert not missing, missing
     lib.dit_abi_version.restype = cint
     assert lib.dit_abi_version() == 3
 
 
+def test_probe_library_exports_every_declared_function():
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libdit_probe.so not built")
+    names = declared_functions()
+    assert set(declared_functions(PROBE_HEADERS)) <= set(names)
+    assert exported(PROBE_LIB) == names
+
+
 @pytest.fixture(scope="module")
 def stub(tmp_path_factory):
+    san = sanitizers.sanitized_dir()
     d = tmp_path_factory.mktemp("stub")
-    so = str(d / "libdit_hoststub.so")
+    so = os.path.join(san, "libstub.so") if san else str(d / "libdit_hoststub.so")
     cmd = ["/opt/rocm/bin/hipcc", "-std=c++17", "-O1", "-fPIC", "-shared",
            "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", CSRC,
-           os.path.join(CSRC, "dit_abi.cpp"), os.path.join(ROOT, "tests", "host_stub.cpp"),
-           "-o", so]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr
+           os.path.join(CSRC, "dit_abi.cpp"), os.path.join(CSRC, "dit_probe_abi.cpp"),
+           os.path.join(ROOT, "tests", "host_stub.cpp"), "-o", so]
+    if not san:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
     lib = ctypes.CDLL(so)
     lib.dit_status_reason.restype = ctypes.c_char_p
     lib.dit_ln_modulate.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, f32, cint, vp]
@@ -466,3 +491,112 @@ def test_modulate_scale_shift_guards(stub):
         assert mod(stub, **kw) == status, kw
         assert why.lower() in stub.dit_status_reason().decode().lower(), kw
     assert r.calls == n1
+
+
+# ---------------------------------------------------------------------------------------
+# Extents beyond the address space: rejected before any other stride arithmetic
+# ---------------------------------------------------------------------------------------
+
+BIG_ROWS, BIG_RS = 1 << 32, 1 << 40         # (rows - 1) * rs * 2 is about 2^73 bytes
+TOP = (1 << 64) - (1 << 20)                  # 1 MiB below the end of the address space
+
+
+def _all_row_ops(stub, rows, rs, x=X, out=OUT, res=RES, y=Y, mod_rows=1, dim=512):
+    """Calls every row-shaped entry point with row tensors of `rows` rows at
+    row stride `rs` (modulation per batch, one row)."""
+    q8 = Q8
+    calls = {
+        "ln_modulate": lambda: stub.dit_ln_modulate(out, rs, x, rs, SC, SH, 512, mod_rows, rows,
+                                                    dim, 1e-6, 0, None),
+        "rmsnorm_scale": lambda: stub.dit_rmsnorm_scale(out, rs, x, rs, W, SC, 512, mod_rows,
+                                                        rows, dim, 1e-6, 0, None),
+        "rmsnorm_tanh_residual": lambda: stub.dit_rmsnorm_tanh_residual(
+            out, rs, x, rs, res, rs, W, G, 512, mod_rows, rows, dim, 1e-6, 0, None),
+        "residual_gate_add": lambda: stub.dit_residual_gate_add(out, rs, res, rs, y, rs, G, 512,
+                                                                mod_rows, rows, dim, 0, None),
+        "modulate_scale_shift": lambda: mod(stub, out=out, out_rs=rs, x=x, x_rs=rs,
+                                            mod_rows=mod_rows, rows=rows, dim=dim),
+        "gate_add_ln_modulate": lambda: gate_ln(stub, out_res=out, out_res_rs=rs, out=A * 10,
+                                                out_rs=rs, res=res, res_rs=rs, y=y, y_rs=rs,
+                                                mod_rows=mod_rows, rows=rows, dim=dim),
+        "ln_modulate_fp8": lambda: stub.dit_ln_modulate_fp8(out, rs, q8, rs, x, rs, SC, SH, 512,
+                                                            mod_rows, rows, dim, 1e-6, FS, 0,
+                                                            None),
+        "gate_add_ln_modulate_fp8": lambda: stub.dit_gate_add_ln_modulate_fp8(
+            out, rs, A * 10, rs, q8, rs, res, rs, y, rs, G, SC, SH, 512, mod_rows, rows, dim,
+            1e-6, FS, 0, None),
+    }
+    return {k: f() for k, f in calls.items()}
+
+
+def test_huge_row_extent_rejected_by_every_row_entry_point(stub):
+    """rows = 2^32 at row stride 2^40 describes about 2^73 bytes: every row
+    entry point refuses it (DIT_ERR_INVALID) and launches nothing."""
+    r = Rec(stub)
+    n0 = r.calls
+    for name, st in _all_row_ops(stub, BIG_ROWS, BIG_RS).items():
+        assert st == INVALID, name
+        assert "extent" in stub.dit_status_reason().decode(), name
+    assert r.calls == n0
+
+
+def test_row_stride_at_int64_limit_rejected(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    for name, st in _all_row_ops(stub, 2, (1 << 63) - 8).items():
+        assert st == INVALID, name
+    assert r.calls == n0
+
+
+def test_single_row_ignores_its_stride(stub):
+    """With one row the stride never enters an address: any value is fine."""
+    r = Rec(stub)
+    n0 = r.calls
+    for name, st in _all_row_ops(stub, 1, (1 << 63) - 8).items():
+        assert st == OK, name
+    assert r.calls == n0 + 8
+
+
+def test_tensor_running_past_the_address_space_rejected(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    for name, st in _all_row_ops(stub, 8, 1 << 17, x=TOP, res=TOP, y=TOP).items():  # 256 KiB rows
+        assert st == INVALID, name
+    assert r.calls == n0
+    assert ln(stub, x=TOP, x_rs=512, rows=8, dim=512) == OK            # 8 KiB fits
+
+
+def test_qkv_huge_extents_rejected(stub):
+    r = Rec(stub)
+    txt, img = _streams()
+    H, Dh, S = 24, 128, 4608
+    base = A * 512
+    n0 = r.calls
+    big = Stream(img.q, img.k, img.v, 1 << 40, 1 << 60, img.q_weight, img.k_weight, 1 << 32)
+    assert _qkv(stub, txt, big, base, base + A * 64, base + A * 128, H * Dh,
+                S * H * Dh) in (INVALID, UNSUPPORTED)
+    wide = Stream(img.q, img.k, img.v, 1 << 40, 1 << 60, img.q_weight, img.k_weight, 4096)
+    assert _qkv(stub, txt, wide, base, base + A * 64, base + A * 128, H * Dh,
+                S * H * Dh) == INVALID
+    assert "extent" in stub.dit_status_reason().decode()
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, 1 << 40,
+                1 << 60) == INVALID                          # output strides
+    huge = Stream(img.q, img.k, img.v, img.tok_stride, img.batch_stride, img.q_weight,
+                  img.k_weight, (1 << 63) - 1)               # token counts that overflow
+    assert _qkv(stub, huge, huge, base, base + A * 64, base + A * 128, H * Dh,
+                S * H * Dh) == UNSUPPORTED
+    assert _qkv(stub, txt, img, base, base + A * 64, base + A * 128, H * Dh, S * H * Dh,
+                batch=1 << 40) == UNSUPPORTED
+    assert _qkv_dest(stub, txt, img, base, base + 2 * 6 * Dh, base + 4 * 6 * Dh, 3 * 6 * Dh,
+                     S * 3 * 6 * Dh, 6, 1 << 61) == INVALID   # destination stride
+    assert r.calls == n0
+
+
+def test_wan_table_and_probes_past_the_address_space_rejected(stub):
+    r = Rec(stub)
+    n0 = r.calls
+    assert stub.dit_wan_modulation_table(TOP, A * 2, A * 3, 1, 75600, 6, 5120, None) == INVALID
+    assert stub.dit_probe_copy(TOP, A * 2, 1 << 21, 0, None) == INVALID
+    assert stub.dit_probe_unary(0, TOP, A * 2, 1 << 20, 0, None) == INVALID
+    assert stub.dit_probe_fp8(0, A * 2, TOP, 1 << 20, None, None) == INVALID
+    assert r.calls == n0
