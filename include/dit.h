@@ -51,8 +51,13 @@
  *   sums use the order R(D) below.  The output is bit-for-bit deterministic.
  *   DIT_MODE_FAST: hardware reciprocal square root, fused multiply-add inside
  *   the sums and the RoPE products; every bf16 rounding point of the
- *   lossless chain is kept, and tanh(gate) is the same exact table value.  The hardware rsqrt reads a
- *   subnormal argument as zero (result +inf); the norms only reach that with
+ *   lossless chain is kept, and tanh(gate) is the same exact table value.
+ *   The native-bf16 RMSNorm rounds its rstd to bf16 and takes the hardware
+ *   value only where it is not within 4 binary32 steps of a bf16 rounding
+ *   midpoint (else the IEEE quotient), so its bf16 rstd -- and with it
+ *   dit_rmsnorm_scale and dit_rmsnorm_tanh_residual -- is the same in both
+ *   modes.  Elsewhere the hardware rsqrt reads a subnormal argument as zero
+ *   (result +inf); LayerNorm and the Q/K norm only reach that with
  *   eps < 2^-126.
  * Reduction order R(D) (D <= 8192, D % 8 == 0).  A 64-lane wave holds one
  *   row; lane l owns elements 512c + 8l + j (j = 0..7) of chunk c.  Each lane
@@ -135,7 +140,7 @@ dit_status_t dit_ln_modulate(void *out, int64_t out_rs, const void *x, int64_t x
  *   t_i  = bf(x_i * x_i)
  *   ms   = bf((sum_R t) / D)
  *   v    = bf(ms + eps)
- *   rstd = bf(1 / sqrt(v))                         (hardware rsqrt in FAST)
+ *   rstd = bf(1 / sqrt(v))                         (same bf16 value in FAST)
  *   y2_i = bf( bf(x_i * rstd) * w_i )
  *   out  = bf(y2 * scale[m])
  * weight: [dim], contiguous.  scale: [mod_rows, dim], row stride mod_rs.
@@ -154,7 +159,8 @@ dit_status_t dit_rmsnorm_scale(void *out, int64_t out_rs, const void *x, int64_t
  * residual: [rows, dim], row stride res_rs.  gate: [mod_rows, dim].
  * tau is taken from a 736-entry table of correctly rounded values (built per
  * workgroup in LDS) for 2^-4 <= |gate| < 3.5; tau = gate below that range and
- * +-1 above it, both exact.  FAST mode differs only in the rsqrt (as above).
+ * +-1 above it, both exact.  Both modes give the same result (the bf16 rstd
+ * is the same, above).
  */
 dit_status_t dit_rmsnorm_tanh_residual(void *out, int64_t out_rs, const void *x, int64_t x_rs,
                                        const void *residual, int64_t res_rs, const void *weight,

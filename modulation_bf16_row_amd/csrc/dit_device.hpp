@@ -164,6 +164,24 @@ __device__ __forceinline__ float rsqrt_mode(float v) {
   return __builtin_amdgcn_rsqf(v);
 }
 
+// bf16 rstd of the native-bf16 RMSNorm: bf(1 / sqrt(v)) for a bf16 v.
+// FAST takes the hardware reciprocal square root and keeps it unless its
+// binary32 result lies within 4 steps of a bf16 rounding midpoint (low half
+// 0x8000), or v is not a positive normal number; there the IEEE square root
+// and division decide (a rounding test in the manner of Ziv).  The hardware
+// result and the IEEE two-step one each lie within a step of the exact
+// value, so away from the midpoints they round to the same bf16, and the
+// bf16 rstd is the same in both modes -- checked on all 65536 bf16 inputs.
+// One evaluation per row, so the test costs nothing measurable.
+template <int MODE>
+__device__ __forceinline__ float rstd_bf16(float v) {
+  if (MODE == kLossless) return round1(1.0f / __builtin_sqrtf(v));
+  float r = __builtin_amdgcn_rsqf(v);
+  const uint32_t low = __float_as_uint(r) & 0xFFFFu;
+  if (low - 0x7FFCu <= 8u || !(v >= 1.17549435e-38f)) r = 1.0f / __builtin_sqrtf(v);
+  return round1(r);
+}
+
 // ---------------------------------------------------------------------------
 // 128-bit vectors of eight bf16 values.
 // ---------------------------------------------------------------------------

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k_probe_unary(int op, uint16_t *out, cons
   if (op == 0)
     r = round1(1.0f + v);
   else if (op == 2)
-    r = round1(rsqrt_mode<MODE>(v));
+    r = rstd_bf16<MODE>(v);
   else
     r = tanh_lookup(v, tab);
   out[i] = (uint16_t)(__float_as_uint(r) >> 16);

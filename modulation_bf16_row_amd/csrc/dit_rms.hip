@@ -24,7 +24,7 @@ __device__ __forceinline__ float rms_rstd(const V8 (&xv)[NC], int lane, int dim,
       }
   const float ms = round1(wave_sum(p) / (float)dim);     // bf16 mean square
   const float v = round1(ms + eps);                      // bf16 (ms + eps)
-  return round1(rsqrt_mode<MODE>(v));                    // bf16 rstd
+  return rstd_bf16<MODE>(v);                              // bf16 rstd
 }
 
 // y2 = bf(bf(x * rstd) * w) for the pair in word xw (weights w0, w1).

@@ -140,3 +140,23 @@ def chain_block(seed_base=5000, batch=2, tokens=4608, dim=3072):
         weight=uniform_bf16((dim,), 0.5, 1.5, seed_base + 5),
         eps=1e-6,
     )
+
+
+def wan_720p_block_device(seed=4000, tokens=75600, dim=5120, device="cuda"):
+    """The Wan 720p block drawn on the device (host draws of 774 MB tensors
+    take most of a minute): torch's seeded generator on `device`, float32
+    N(0, 1) rows (x, residual), N(0, 0.1) per-token scale/shift/gate and a
+    per-batch gate [1, dim], U(0.5, 1.5) weight, each rounded to bfloat16
+    (nearest even).  Returns bfloat16 device tensors; the oracle receives the
+    same values copied to the host."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+
+    def bf(shape, std):
+        return (torch.randn(shape, device=device, generator=gen) * std).to(torch.bfloat16)
+
+    out = dict(x=bf((tokens, dim), 1.0), residual=bf((tokens, dim), 1.0),
+               scale=bf((tokens, dim), 0.1), shift=bf((tokens, dim), 0.1),
+               gate=bf((tokens, dim), 0.1), gate1=bf((1, dim), 0.1))
+    out["weight"] = (torch.rand(dim, device=device, generator=gen) + 0.5).to(torch.bfloat16)
+    out["eps"] = 1e-6
+    return out
