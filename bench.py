@@ -713,6 +713,11 @@ def _timed_steps(m, torch, plans, steps, kernels):
     return us, e0.elapsed_time(e1)
 
 
+def _progress(msg):
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"[bench] {time.strftime('%H:%M:%S')} {msg}", file=sys.stderr, flush=True)
+
+
 def _kernel_stats(k, us_list):
     us = float(np.mean(us_list))
     gbs = BYTES[k] / (us * 1e-6) / 1e9
@@ -766,6 +771,7 @@ def main():
             plans[args.mode][i % 2][k]()
     torch.cuda.synchronize()
 
+    _progress(f"inputs resident; {args.warmup} warm-up steps done")
     # Timed region: exactly K steps, launched eagerly from prepared calls; every
     # dispatch records its own start/stop events (hipExtLaunchKernelGGL), so the
     # per-kernel durations -- and `value`, LN + AdaLN modulate's bandwidth --
@@ -775,6 +781,7 @@ def main():
     wall = time.perf_counter() - t_wall
     ms_step = region_ms / args.steps
     per_kernel = {k: _kernel_stats(k, samples[k]) for k in KERNELS}
+    _progress(f"timed region: {args.steps} steps, {ms_step:.4f} ms per step")
 
     # The same step as the production launch path would run it: one HIP graph
     # per buffer set (the product library's calls), K replays.
@@ -838,11 +845,14 @@ def main():
                   kernel_sum_ms=round(sum(per_kernel[k]["us"] for k in KERNELS) / 1000.0, 4)),
     )
     if not args.only_step:
-        result.update(
-            kernels_alone=time_alone(m, torch, sets + extra, args.mode),
-            producers=time_producers(m, torch, sets + extra, args.mode, args.steps),
-            wan720p=time_wan(m, torch, args.mode),
-            fast_mode=fast_mode_report(m, torch, sets[1]))
+        _progress("graph replays and the other mode done; kernels alone")
+        result["kernels_alone"] = time_alone(m, torch, sets + extra, args.mode)
+        _progress("producers")
+        result["producers"] = time_producers(m, torch, sets + extra, args.mode, args.steps)
+        _progress("Wan 720p shapes")
+        result["wan720p"] = time_wan(m, torch, args.mode)
+        _progress("FAST against LOSSLESS")
+        result["fast_mode"] = fast_mode_report(m, torch, sets[1])
         wl = result["wan720p"]["ln_modulate_per_token"]
         result["roofline_wan720p"] = dict(
             bound="hbm", achieved=wl["gbs"], peak=PEAK_GBS, unit="GB/s",
@@ -857,6 +867,7 @@ def main():
         result["bit_exact"] = None
         result["bit_exact_note"] = "not checked: the oracle leg was skipped (--no-cpu/--only-step)"
     else:
+        _progress("CPU oracle baseline")
         base, exact = cpu_baseline(blk, qkv, gpu_out)
         result["cpu_baseline"] = base
         if args.mode == "lossless":

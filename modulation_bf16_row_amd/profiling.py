@@ -3,11 +3,13 @@
   python -m modulation_bf16_row_amd.profiling trace RESULTS.db OUT.txt --command "..."
       per-kernel dispatch statistics from a --kernel-trace run
   python -m modulation_bf16_row_amd.profiling traffic FETCH.db WRITE.db OUT.txt \
-        --kernel k_ln_modulate [--grid N] --calib k_probe_copy --calib-bytes 1073741824 \
-        --command "..."
+        --kernel k_ln_modulate [--grid N] --calib 'k_probe_copy<3>' \
+        --calib-default 'k_probe_copy<2>' --calib-bytes 1073741824 --command "..."
       HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE runs,
       each scaled by what the same counter reads for a copy dispatch of known
-      size (calib-bytes read and calib-bytes written)
+      size (calib-bytes read and calib-bytes written): FETCH_SIZE by the copy
+      with nontemporal loads (--calib) and, for comparison, by the copy with
+      default-policy loads (--calib-default), whose factor is also recorded
 
 The traffic summary records a hash of the code of the kernel's translation
 unit (--source) or of all kernel sources; the benchmark only
@@ -114,7 +116,8 @@ def counter_values(db, counter):
 
 
 def _match(by, pattern, grid=None):
-    keys = [k for k in by if re.search(pattern, k[0]) and (grid is None or k[1] == grid)]
+    keys = [k for k in by if (re.search(pattern, k[0]) or k[0].startswith(pattern))
+            and (grid is None or k[1] == grid)]
     if not keys:
         raise SystemExit(f"no dispatch of {pattern!r} (grid {grid}) in {sorted(by)}")
     vals = [v for k in keys for v in by[k]]
@@ -136,7 +139,7 @@ def write_trace(db, out, command):
 
 
 def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, grid=None,
-                  source=None):
+                  source=None, calib_default=None):
     fetch = counter_values(fetch_db, "FETCH_SIZE")
     write = counter_values(write_db, "WRITE_SIZE")
     f_k, nf = _match(fetch, kernel, grid)
@@ -145,6 +148,12 @@ def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, 
     w_c, _ = _match(write, calib)
     f_scale = calib_bytes / (f_c * 1024.0)
     w_scale = calib_bytes / (w_c * 1024.0)
+    extra = []
+    if calib_default:
+        f_d, _ = _match(fetch, calib_default)
+        extra = [f"calib_default_loads_kernel = {calib_default}",
+                 f"calib_default_loads_fetch_kib = {f_d:.1f}",
+                 f"fetch_scale_default_loads = {calib_bytes / (f_d * 1024.0):.4f}"]
     read_b = f_k * 1024.0 * f_scale
     write_b = w_k * 1024.0 * w_scale
     lines = [
@@ -164,6 +173,7 @@ def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, 
         f"calib_write_kib = {w_c:.1f}",
         f"fetch_scale = {f_scale:.4f}",
         f"write_scale = {w_scale:.4f}",
+        *extra,
         f"hbm_read_bytes_per_launch = {read_b:.0f}",
         f"hbm_write_bytes_per_launch = {write_b:.0f}",
         f"hbm_bytes_per_launch = {read_b + write_b:.0f}",
@@ -187,7 +197,9 @@ def main():
     c.add_argument("write_db")
     c.add_argument("out")
     c.add_argument("--kernel", required=True)
-    c.add_argument("--calib", default="k_probe_copy")
+    c.add_argument("--calib", default="k_probe_copy<3>")
+    c.add_argument("--calib-default", default=None,
+                   help="copy dispatch with default-policy loads (its factor is recorded)")
     c.add_argument("--calib-bytes", type=float, default=float(1 << 30))
     c.add_argument("--grid", type=int, default=None,
                    help="only dispatches of this grid size (work-items)")
@@ -199,7 +211,7 @@ def main():
         write_trace(a.db, a.out, a.command)
     else:
         write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command,
-                      a.grid, a.source)
+                      a.grid, a.source, a.calib_default)
 
 
 if __name__ == "__main__":
