@@ -3,8 +3,12 @@
  * primitives over caller arrays.  They exist so that each primitive can be
  * checked exhaustively (all 65536 bf16 inputs, all 2^32 binary32 inputs)
  * against an independent CPU reference; they are not needed to use the
- * epilogues.  Conventions (ownership, asynchrony, status codes, thread-local
- * reason) are those of dit.h.  n == 0 is a valid empty call.
+ * epilogues, and only the instrumented build, libdit_probe.so (the same
+ * kernel objects as libdit.so plus these and dit_timing.h), exports them.
+ * Conventions (ownership, asynchrony, status codes, thread-local reason) are
+ * those of dit.h; every array's extent is checked as there (DIT_ERR_INVALID
+ * beyond 2^56 bytes or the end of the address space).  n == 0 is a valid
+ * empty call.
  */
 #ifndef DIT_PROBE_H
 #define DIT_PROBE_H

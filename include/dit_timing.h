@@ -1,9 +1,12 @@
 /*
- * dit_timing.h -- kernel timing hook for benchmarks.
+ * dit_timing.h -- kernel timing hook for benchmarks, exported by the
+ * instrumented build libdit_probe.so only (the product library keeps no
+ * timing state).
  *
  * dit_time_next_launch(start, stop) registers two HIP events (created by the
  * caller, e.g. with hipEventCreate) for the calling thread.  The next
- * epilogue or probe call made on that thread that launches a kernel does so
+ * epilogue or probe call into libdit_probe.so made on that thread that
+ * launches a kernel does so
  * with hipExtLaunchKernelGGL, so the dispatch itself records `start` when
  * the kernel begins and `stop` when it ends; hipEventElapsedTime(start,
  * stop) is then the kernel's own duration, without the dispatch overhead
