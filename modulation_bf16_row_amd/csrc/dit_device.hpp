@@ -127,18 +127,30 @@ __device__ __forceinline__ float group16_sum(float p) {
 // after the first workgroups) into LDS.  The exhaustive device test checks
 // every one of the 65536 inputs.
 // ---------------------------------------------------------------------------
+// Four 32-bit words as one 128-bit vector value (loads, stores, asm operands).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr uint32_t kTanhTabLo = 0x3D80u, kTanhTabHi = 0x4060u;
 constexpr int kTanhTabN = (int)(kTanhTabHi - kTanhTabLo);             // 736
 constexpr int kTanhTabVecs = (kTanhTabN * 2 + 15) / 16;               // uint4s
 static_assert(kTanhTabN == kTanhTabEntries && kTanhTabN % 8 == 0, "tanh table size");
 
 // The copy in two halves, so that a kernel can issue other loads between
-// them: thread tid < kTanhTabVecs fetches 16 bytes of the table, then puts
-// them into LDS (tab: 16-byte aligned, kTanhTabVecs uint4s).  The workgroup
-// needs at least kTanhTabVecs threads.
+// them: tanh_table_fetch loads 16 bytes of the table for thread tid (threads
+// past the table reload its first vector, so every thread loads, with no
+// branch), tanh_table_put stores them into LDS for tid < kTanhTabVecs (tab:
+// 16-byte aligned, kTanhTabVecs uint4s; the workgroup needs at least
+// kTanhTabVecs threads).  An empty asm statement that passes the address
+// through keeps the load where it is written: the optimizer would otherwise
+// sink it to its use, past the row loads a kernel issues in between, and as
+// a wave's loads return in order the staging would then wait for the rows.
 __device__ __forceinline__ uint4 tanh_table_fetch(int tid) {
-  return tid < kTanhTabVecs ? reinterpret_cast<const uint4 *>(kTanhTabGlobal)[tid]
-                            : make_uint4(0u, 0u, 0u, 0u);
+  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+  global_u32x4 *p = (global_u32x4 *)(reinterpret_cast<const u32x4 *>(kTanhTabGlobal)) +
+                    (tid < kTanhTabVecs ? tid : 0);
+  asm volatile("" : "+v"(p));
+  const u32x4 t = *p;
+  return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
 __device__ __forceinline__ void tanh_table_put(uint16_t *tab, int tid, uint4 v) {
@@ -194,7 +206,6 @@ struct V8 {
 // loads and stores, which measured 9% faster on a pure copy than the default
 // policy.  Operands shared by many rows (weights, per-batch modulation rows,
 // cos/sin) use the default policy so they stay cached.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ V8 load8(const uint16_t *p) {
   const uint4 u = *reinterpret_cast<const uint4 *>(p);

@@ -28,14 +28,18 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, STAGED ? 3 : 2) void k_
   {
     V8 gg[stage_iters<NC>()], gs[stage_iters<NC>()], gf[stage_iters<NC>()];
     if (STAGED) {
+      // The staging loads, then the first row's, with no branch among them,
+      // so the row arrives while the workgroup stages (dit_rows.hpp,
+      // load_row_nb).
       const int64_t off = sp.m * a.mod_rs;
-      stage_fetch<NC>(gg, a.gate + off, dim);
-      stage_fetch<NC>(gs, a.scale + off, dim);
-      stage_fetch<NC>(gf, a.shift + off, dim);
-    }
-    if (STAGED && sp.begin < sp.end) {
-      load_row<NC, kNtGate>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
-      load_row<NC, kNtGateLnY>(yv, a.y + sp.begin * a.y_rs, lane, dim);
+      stage_fetch_nb<NC>(gg, a.gate + off, dim);
+      stage_fetch_nb<NC>(gs, a.scale + off, dim);
+      stage_fetch_nb<NC>(gf, a.shift + off, dim);
+      phase_barrier();
+      const int64_t r0 = sp.begin < a.rows ? sp.begin : a.rows - 1;   // (in the tensor)
+      load_row_nb<NC, kNtGate>(rv, a.residual + r0 * a.res_rs, lane, dim);
+      load_row_nb<NC, kNtGateLnY>(yv, a.y + r0 * a.y_rs, lane, dim);
+      phase_barrier();
     }
     if (STAGED) {
       stage_each<NC>(dim, [&](int i, int v) {

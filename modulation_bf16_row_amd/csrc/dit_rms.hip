@@ -39,19 +39,57 @@ __device__ __forceinline__ void rms_y2(float &y0, float &y1, uint32_t xw, float 
 }
 
 
-// LDS: [0] = weight (always), [1] = scale (staged), binary32.
+// out = bf(y2 * scale) for the row in xv; chunk c's weight and scale come from
+// the staged rows (binary32) and, unstaged, the scale from sc.
+template <int NC, int MODE, bool STAGED>
+__device__ __forceinline__ void rms_scale_out(const RmsScaleArgs &a, const float4 *lds,
+                                              const V8 (&xv)[NC], const V8 (&sc)[NC],
+                                              int64_t r, int lane, int dim) {
+  constexpr int kRow = stage_vecs<NC>();
+  const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+  phase_barrier();
+  uint16_t *orow = a.out + r * a.out_rs;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (!valid<NC>(c, lane, dim)) continue;
+    float w[8], s[8];
+    stage_get(lds, c, lane, w);
+    if (STAGED)
+      stage_get(lds + kRow, c, lane, s);
+    else
+      unpack8(sc[c], s);
+    V8 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y0, y1;
+      rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
+      o.w[k] = pack(y0 * s[2 * k], y1 * s[2 * k + 1]);
+    }
+    store8(orow + 512 * c + 8 * lane, o);
+  }
+}
+
+// LDS: [0] = weight (always), [1] = scale (staged), binary32.  The staged
+// layout takes one row per wave (four per workgroup): the row's loads are
+// issued, with no branch among them, after the staging loads and before the
+// staging, so the row arrives while the workgroup stages.
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale(RmsScaleArgs a) {
   extern __shared__ float4 lds[];
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   constexpr int kRow = stage_vecs<NC>();
-  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+  const Span sp = STAGED ? mod_spans(a.per_mod, 1, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   if (sp.wg_empty) return;                                 // whole workgroup idle
   V8 gw[stage_iters<NC>()], gs[stage_iters<NC>()], xv[NC];
-  stage_fetch<NC>(gw, a.weight, dim);                      // weight: every launch
-  if (STAGED) stage_fetch<NC>(gs, a.scale + sp.m * a.mod_rs, dim);
-  if (STAGED && sp.begin < sp.end) load_row<NC, kNtRms>(xv, a.x + sp.begin * a.x_rs, lane, dim);
+  stage_fetch_nb<NC>(gw, a.weight, dim);                   // weight: every launch
+  if (STAGED) {
+    stage_fetch_nb<NC>(gs, a.scale + sp.m * a.mod_rs, dim);
+    phase_barrier();                                       // the staging loads first,
+    const int64_t r0 = sp.begin < a.rows ? sp.begin : a.rows - 1;  // (in the tensor)
+    load_row_nb<NC, kNtRms>(xv, a.x + r0 * a.x_rs, lane, dim);
+    phase_barrier();                                       // then the row's
+  }
   stage_each<NC>(dim, [&](int i, int v) {
     float w[8];
     unpack8(gw[i], w);
@@ -62,38 +100,57 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_scale
     }
   });
   __syncthreads();
-
+  if (STAGED) {
+    if (sp.begin < sp.end) rms_scale_out<NC, MODE, true>(a, lds, xv, xv, sp.begin, lane, dim);
+    return;
+  }
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 sc[NC];
-    if (!STAGED || r != sp.begin) load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
-    const int64_t m = STAGED ? sp.m : r / a.per_mod;
-    if (!STAGED) load_mod_row<NC>(sc, a.scale + m * a.mod_rs, lane, dim, a.per_mod == 1);
-    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    phase_barrier();
-    uint16_t *orow = a.out + r * a.out_rs;
+    load_row<NC, kNtRms>(xv, a.x + r * a.x_rs, lane, dim);
+    load_mod_row<NC>(sc, a.scale + (r / a.per_mod) * a.mod_rs, lane, dim, a.per_mod == 1);
+    rms_scale_out<NC, MODE, false>(a, lds, xv, sc, r, lane, dim);
+  }
+}
+
+// RMSNorm-tanh-residual output of the row in xv with residual rv; tanh(gate)
+// comes from the staged row (binary32) or, unstaged, from the table lookup
+// of the gate vectors tau.
+template <int NC, int MODE, bool STAGED>
+__device__ __forceinline__ void tanh_out(const RmsTanhArgs &a, const float4 *lds,
+                                         const uint16_t *tab, const V8 (&xv)[NC],
+                                         const V8 (&rv)[NC], const V8 (&tau)[NC], int64_t r,
+                                         int lane, int dim) {
+  constexpr int kRow = stage_vecs<NC>();
+  const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
+  phase_barrier();
+  uint16_t *orow = a.out + r * a.out_rs;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!valid<NC>(c, lane, dim)) continue;
-      float w[8], s[8];
-      stage_get(lds, c, lane, w);
-      if (STAGED)
-        stage_get(lds + kRow, c, lane, s);
-      else
-        unpack8(sc[c], s);
-      V8 o;
+  for (int c = 0; c < NC; ++c) {
+    if (!valid<NC>(c, lane, dim)) continue;
+    float w[8], tg[8];
+    stage_get(lds, c, lane, w);
+    if (STAGED) {
+      stage_get(lds + kRow, c, lane, tg);
+    } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float y0, y1;
-        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
-        o.w[k] = pack(y0 * s[2 * k], y1 * s[2 * k + 1]);
-      }
-      store8(orow + 512 * c + 8 * lane, o);
+      for (int j = 0; j < 8; ++j) tg[j] = tanh_lookup(elem(tau[c], j), tab);
     }
+    V8 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y0, y1;
+      rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
+      float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
+      round2(q0, q1);                                   // bf(tanh(gate) * y2)
+      o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
+    }
+    store8(orow + 512 * c + 8 * lane, o);
   }
 }
 
 // LDS: [0] = weight (always), [1] = tanh(gate) (staged), binary32; then the
-// tanh table.  tanh comes from the table in both modes.
+// tanh table.  tanh comes from the table in both modes.  The staged layout
+// takes one row per wave, loaded as in k_rmsnorm_scale.
 template <int NC, int MODE, bool STAGED>
 __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_residual(
     RmsTanhArgs a) {
@@ -101,16 +158,19 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
   const int lane = threadIdx.x & 63, dim = (int)a.dim;
   constexpr int kRow = stage_vecs<NC>();
   uint16_t *tab = reinterpret_cast<uint16_t *>(lds + (STAGED ? 2 : 1) * kRow);
-  const Span sp = STAGED ? mod_spans(a.per_mod, a.rows_per_wave, a.blocks_per_mod)
+  const Span sp = STAGED ? mod_spans(a.per_mod, 1, a.blocks_per_mod)
                          : spans(a.rows, a.rows_per_wave);
   if (sp.wg_empty) return;                                 // whole workgroup idle
   V8 gw[stage_iters<NC>()], gg[stage_iters<NC>()], xv[NC], rv[NC];
   const uint4 tv = tanh_table_fetch(threadIdx.x);
-  stage_fetch<NC>(gw, a.weight, dim);                      // weight: every launch
-  if (STAGED) stage_fetch<NC>(gg, a.gate + sp.m * a.mod_rs, dim);
-  if (STAGED && sp.begin < sp.end) {
-    load_row<NC, kNtTanh>(xv, a.x + sp.begin * a.x_rs, lane, dim);
-    load_row<NC, kNtTanh>(rv, a.residual + sp.begin * a.res_rs, lane, dim);
+  stage_fetch_nb<NC>(gw, a.weight, dim);                   // weight: every launch
+  if (STAGED) {
+    stage_fetch_nb<NC>(gg, a.gate + sp.m * a.mod_rs, dim);
+    phase_barrier();                                       // the staging loads first,
+    const int64_t r0 = sp.begin < a.rows ? sp.begin : a.rows - 1;  // (in the tensor)
+    load_row_nb<NC, kNtTanh>(xv, a.x + r0 * a.x_rs, lane, dim);
+    load_row_nb<NC, kNtTanh>(rv, a.residual + r0 * a.res_rs, lane, dim);
+    phase_barrier();                                       // then the row's
   }
   tanh_table_put(tab, threadIdx.x, tv);
   stage_each<NC>(dim, [&](int i, int v) {
@@ -127,41 +187,15 @@ __global__ __launch_bounds__(kThreads) DIT_OCCUPANCY(NC, 3) void k_rmsnorm_tanh_
       stage_put(lds + kRow, v, t);
     });
     __syncthreads();
+    if (sp.begin < sp.end) tanh_out<NC, MODE, true>(a, lds, tab, xv, rv, xv, sp.begin, lane, dim);
+    return;
   }
-
   for (int64_t r = sp.begin; r < sp.end; ++r) {
     V8 tau[NC];
-    if (!STAGED || r != sp.begin) {
-      load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
-      load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
-    }
-    const int64_t m = STAGED ? sp.m : r / a.per_mod;
-    if (!STAGED) load_mod_row<NC>(tau, a.gate + m * a.mod_rs, lane, dim, a.per_mod == 1);
-    const float rstd = rms_rstd<NC, MODE>(xv, lane, dim, a.eps);
-    phase_barrier();
-    uint16_t *orow = a.out + r * a.out_rs;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (!valid<NC>(c, lane, dim)) continue;
-      float w[8], tg[8];
-      stage_get(lds, c, lane, w);
-      if (STAGED) {
-        stage_get(lds + kRow, c, lane, tg);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tg[j] = tanh_lookup(elem(tau[c], j), tab);
-      }
-      V8 o;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float y0, y1;
-        rms_y2(y0, y1, xv[c].w[k], w[2 * k], w[2 * k + 1], rstd);
-        float q0 = tg[2 * k] * y0, q1 = tg[2 * k + 1] * y1;
-        round2(q0, q1);                                   // bf(tanh(gate) * y2)
-        o.w[k] = pack(lo(rv[c].w[k]) + q0, hi(rv[c].w[k]) + q1);
-      }
-      store8(orow + 512 * c + 8 * lane, o);
-    }
+    load_row<NC, kNtTanh>(xv, a.x + r * a.x_rs, lane, dim);
+    load_row<NC, kNtTanh>(rv, a.residual + r * a.res_rs, lane, dim);
+    load_mod_row<NC>(tau, a.gate + (r / a.per_mod) * a.mod_rs, lane, dim, a.per_mod == 1);
+    tanh_out<NC, MODE, false>(a, lds, tab, xv, rv, tau, r, lane, dim);
   }
 }
 
