@@ -600,3 +600,20 @@ def test_wan_table_and_probes_past_the_address_space_rejected(stub):
     assert stub.dit_probe_unary(0, TOP, A * 2, 1 << 20, 0, None) == INVALID
     assert stub.dit_probe_fp8(0, A * 2, TOP, 1 << 20, None, None) == INVALID
     assert r.calls == n0
+
+
+def test_c_abi_check_program_builds_and_links(tmp_path):
+    """The C-ABI check program compiles against include/*.h with the host
+    compiler alone and links libdit.so and liboracle.so."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "dit_c_check_build", os.path.join(os.path.dirname(__file__), "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    if not (os.path.exists(os.path.join(mod.PKG, "libdit.so"))
+            and os.path.exists(os.path.join(mod.ORACLE, "liboracle.so"))):
+        pytest.skip("libdit.so / liboracle.so not built")
+    out = mod.build(out=str(tmp_path / "dit_c_check"))
+    res = subprocess.run(["ldd", out], capture_output=True, text=True)
+    assert "libdit.so" in res.stdout and "liboracle.so" in res.stdout
+    assert "not found" not in res.stdout
