@@ -83,7 +83,8 @@ def kernel_source_hash(source=None):
 def _short(name):
     """Kernel name without return type, namespace and parameter list; template
     arguments are kept (for the row kernels: chunks, mode (0 = lossless,
-    1 = fast), staged)."""
+    1 = fast), and for the LayerNorm producers whether the E4M3 copy is
+    written)."""
     name = re.sub(r"\(.*$", "", name).strip()
     return re.sub(r"^void ", "", name).replace("dit::", "")
 
