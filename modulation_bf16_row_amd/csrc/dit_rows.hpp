@@ -21,8 +21,10 @@
 // gate, bf(1 + scale) and shift -- and the waves read them with two 128-bit LDS accesses per
 // 8-element vector, with no bf16 unpacking in the row loop (the kernels
 // are close to their vector-ALU budget, so every instruction per element
-// counts).  With per-token modulation rows are laid out consecutively and
-// each row's operands are loaded (and transformed) by the wave using them.
+// counts).  Without the staged layout (per-token modulation) LayerNorm, the
+// gated residual + LN producer and RMSNorm-scale split each row over several
+// waves (dit_split.hpp); RMSNorm-tanh-residual lays its rows out
+// consecutively, one per wave, and each wave loads its row's gate row.
 //
 // Sums follow R(dim): each lane adds its own terms in (chunk, element)
 // order, then a fixed xor butterfly across the 64 lanes.
@@ -241,8 +243,9 @@ __device__ __forceinline__ Span mod_spans(int64_t per_mod, int64_t rpw, int64_t 
 //   noise.  Per-batch modulation (at least one workgroup's worth of rows per
 //   modulation row) takes the staged layout: blocks_per_mod workgroups per
 //   modulation row, each converting its modulation operands into LDS once.
-//   Otherwise (per-token modulation) rows are laid out consecutively and
-//   each wave loads them.
+//   Otherwise the kernels take the split-row layout (dit_split.hpp), except
+//   RMSNorm-tanh-residual, whose rows are laid out consecutively, one per
+//   wave, each wave loading its row's operands.
 // ---------------------------------------------------------------------------
 
 // Staging several binary32 rows stops paying once it limits the workgroups

@@ -1,6 +1,7 @@
-// dit_split.hpp -- the split-row layout of the row kernels (dit_ln.hip,
-// dit_gate_ln.hip, dit_rms.hip), taken where each row carries its own
-// modulation row (per-token modulation) and the staged layout does not apply.
+// dit_split.hpp -- the split-row layout of the row kernels (LayerNorm + AdaLN,
+// the gated residual + LN producer, RMSNorm-scale), taken where the staged
+// layout of dit_rows.hpp does not apply (per-token modulation, or too few rows
+// per modulation row).
 //
 // Layout.  One workgroup per row at a time, W = ceil(NC / 2) waves; wave w
 // moves chunks 2w and 2w + 1 of the row (1 KiB each per operand, the same
@@ -12,8 +13,8 @@
 // chunks and 480 us when it moves one, independent of the order in which a
 // wave walks its chunks.  Two chunks per wave balance the short bursts
 // against the rows a CU keeps in flight (a row ties up W waves, and at most
-// 32 waves are resident per CU): one chunk per wave ran the LayerNorm
-// 25% slower than two, three or five chunks 5-8% slower.
+// 32 waves are resident per CU): at that shape one chunk per wave ran the
+// LayerNorm about 30% slower than two, three or five chunks 5-8% slower.
 //
 // The sum order is unchanged.  The reduction of a row needs, for each lane
 // l, its terms in (chunk, element) order, a chain that runs through every
@@ -21,9 +22,9 @@
 // chunk) to LDS, wave 0 runs the chains of order R over the published row
 // and the fixed butterfly, and leaves the row's statistics in LDS for all
 // waves.  Each wave keeps its own chunks in registers for the output.  The
-// register budget is 8 waves per SIMD (64 VGPRs): with the budget the
-// compiler picks by itself (84 VGPRs for RMSNorm-tanh-residual), the CU holds
-// fewer rows and the same kernel ran 25% slower.
+// register budget is 8 waves per SIMD (64 VGPRs): a split kernel left at the
+// compiler's own choice of 84 VGPRs holds fewer rows per CU and ran 25%
+// slower than the same code at 64.
 //
 // Every load is issued with its index clamped into the tensor (chunks past
 // the row reload element 0, whose values are never used), so the loads carry
