@@ -614,6 +614,21 @@ def _bf16_values(h):
         return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def fast_targets(res, ops):
+    """FAST-mode targets against LOSSLESS, each met or not: at most 2 bf16
+    steps literally on every output, at least 99.9% of elements within one
+    step, and at least 40 dB PSNR after the chain (identical runs, PSNR None,
+    meet it)."""
+    over = [k for k in ops if res[k]["max_ulp"] > 2]
+    psnr = res["chain"]["psnr_db"]
+    return {
+        "max_2_steps_literal": dict(met=not over, over=over),
+        "within_1_step_at_least_99.9pct": dict(
+            met=all(res[k]["frac_within_1ulp"] >= 0.999 for k in ops)),
+        "chain_psnr_at_least_40_db": dict(met=psnr is None or psnr >= 40.0),
+    }
+
+
 def fast_mode_report(m, torch, s, chain_iters=50):
     """FAST against LOSSLESS: on one buffer set, for each step output, the
     largest distance in bf16 steps and the fraction of elements within one
@@ -656,9 +671,11 @@ def fast_mode_report(m, torch, s, chain_iters=50):
     rng = float(ref.max() - ref.min())
     res["chain"] = dict(iterations=chain_iters, shape=list(w["x"].shape),
                         psnr_db=None if mse == 0 else round(10 * np.log10(rng * rng / mse), 2))
+    res["targets"] = fast_targets(res, list(outs["lossless"]))
     res["note"] = ("max_ulp is the literal distance; under cancellation in the last addition "
                    "it can exceed the bound that holds in steps of the magnitude entering "
-                   "that rounding (checked by the tests)")
+                   "that rounding (checked by the tests), so the literal 2-step target is "
+                   "reported as not met wherever max_ulp > 2")
     return res
 
 

@@ -53,3 +53,20 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_fast_targets_mark_the_literal_two_step_bound():
+    import bench
+    res = {"ln": dict(max_ulp=4, frac_within_1ulp=0.999999),
+           "rms": dict(max_ulp=0, frac_within_1ulp=1.0),
+           "chain": dict(psnr_db=189.9)}
+    t = bench.fast_targets(res, ["ln", "rms"])
+    assert t["max_2_steps_literal"] == dict(met=False, over=["ln"])
+    assert t["within_1_step_at_least_99.9pct"]["met"] is True
+    assert t["chain_psnr_at_least_40_db"]["met"] is True
+    res["ln"] = dict(max_ulp=2, frac_within_1ulp=0.998)
+    res["chain"] = dict(psnr_db=39.0)
+    t = bench.fast_targets(res, ["ln", "rms"])
+    assert t["max_2_steps_literal"]["met"] is True
+    assert t["within_1_step_at_least_99.9pct"]["met"] is False
+    assert t["chain_psnr_at_least_40_db"]["met"] is False
