@@ -614,18 +614,29 @@ def _bf16_values(h):
         return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _json_scalar(v):
+    """numpy scalars in the result line as plain JSON values."""
+    if isinstance(v, np.bool_):
+        return bool(v)
+    if isinstance(v, np.integer):
+        return int(v)
+    if isinstance(v, np.floating):
+        return float(v)
+    raise TypeError(f"{type(v).__name__} is not JSON serializable")
+
+
 def fast_targets(res, ops):
     """FAST-mode targets against LOSSLESS, each met or not: at most 2 bf16
     steps literally on every output, at least 99.9% of elements within one
     step, and at least 40 dB PSNR after the chain (identical runs, PSNR None,
     meet it)."""
-    over = [k for k in ops if res[k]["max_ulp"] > 2]
+    over = [k for k in ops if int(res[k]["max_ulp"]) > 2]
     psnr = res["chain"]["psnr_db"]
     return {
-        "max_2_steps_literal": dict(met=not over, over=over),
+        "max_2_steps_literal": dict(met=bool(not over), over=over),
         "within_1_step_at_least_99.9pct": dict(
-            met=all(res[k]["frac_within_1ulp"] >= 0.999 for k in ops)),
-        "chain_psnr_at_least_40_db": dict(met=psnr is None or psnr >= 40.0),
+            met=bool(all(float(res[k]["frac_within_1ulp"]) >= 0.999 for k in ops))),
+        "chain_psnr_at_least_40_db": dict(met=bool(psnr is None or float(psnr) >= 40.0)),
     }
 
 
@@ -899,7 +910,7 @@ def main():
         else:
             result["bit_exact"] = None
             result["bit_exact_note"] = "FAST mode is not bit-exact by design"
-    print(json.dumps(result), flush=True)
+    print(json.dumps(result, default=_json_scalar), flush=True)
 
 
 if __name__ == "__main__":

@@ -70,3 +70,22 @@ def test_fast_targets_mark_the_literal_two_step_bound():
     assert t["max_2_steps_literal"]["met"] is True
     assert t["within_1_step_at_least_99.9pct"]["met"] is False
     assert t["chain_psnr_at_least_40_db"]["met"] is False
+
+
+def test_fast_targets_serialize_with_numpy_inputs():
+    import json
+    import bench
+    res = {"ln": dict(max_ulp=np.int64(4), frac_within_1ulp=np.float64(0.999999)),
+           "chain": dict(psnr_db=np.float64(189.86))}
+    t = bench.fast_targets(res, ["ln"])
+    back = json.loads(json.dumps(t))
+    assert back["max_2_steps_literal"] == {"met": False, "over": ["ln"]}
+    assert back["chain_psnr_at_least_40_db"]["met"] is True
+
+
+def test_result_line_serializes_numpy_scalars():
+    import json
+    import bench
+    line = json.dumps({"a": np.bool_(True), "b": np.int64(3), "c": np.float32(0.5)},
+                      default=bench._json_scalar)
+    assert json.loads(line) == {"a": True, "b": 3, "c": 0.5}
