@@ -11,6 +11,15 @@
       with nontemporal loads (--calib) and, for comparison, by the copy with
       default-policy loads (--calib-default), whose factor is also recorded
 
+  python -m modulation_bf16_row_amd.profiling clock RESULTS.db OUT.txt --command "..."
+      per kernel, from a --pmc GRBM_COUNT run: the effective core clock of
+      each dispatch of 200 us or more (GRBM_COUNT, summed over the XCDs, /
+      XCDs / duration),
+      the core cycles it took (clock x duration), and how closely duration
+      follows the clock across dispatches (a correlation near -1 means a
+      fixed number of core cycles: the dispatch is bound by the core clock,
+      not by HBM)
+
 The traffic summary records a hash of the code of the kernel's translation
 unit (--source) or of all kernel sources; the benchmark only
 reports it while the sources still match.
@@ -186,6 +195,53 @@ def write_traffic(fetch_db, write_db, out, kernel, calib, calib_bytes, command, 
     print("\n".join(lines))
 
 
+def _pearson(xs, ys):
+    mx, my = statistics.mean(xs), statistics.mean(ys)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    sxx = sum((x - mx) ** 2 for x in xs)
+    syy = sum((y - my) ** 2 for y in ys)
+    return sxy / (sxx * syy) ** 0.5 if sxx > 0 and syy > 0 else float("nan")
+
+
+def clock_stats(db, xcds=8, min_us=200.0):
+    """Per (kernel, grid): dispatches, median duration (us), median effective
+    clock (GHz), median core cycles (thousands: us x GHz), and the correlation of
+    duration with clock, over dispatches of at least min_us."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, kernel_name, grid_size, value, duration from "
+                       "counters_collection where counter_name = 'GRBM_COUNT'").fetchall()
+    by = {}
+    for _, name, grid, v, dur in rows:
+        if dur and dur / 1000.0 >= min_us:
+            by.setdefault((_short(name), int(grid)), []).append((dur / 1000.0, v / xcds / dur))
+    out = []
+    for (name, grid), pts in by.items():
+        if len(pts) < 4:
+            continue
+        d = [p[0] for p in pts]
+        c = [p[1] for p in pts]
+        cyc = [a * b for a, b in pts]
+        out.append((name, grid, len(pts), statistics.median(d), statistics.median(c), min(c),
+                    max(c), statistics.median(cyc), _pearson(d, c)))
+    return sorted(out, key=lambda r: -r[2] * r[3])
+
+
+def write_clock(db, out, command):
+    lines = ["# effective core clock per dispatch from rocprofv3 --pmc GRBM_COUNT "
+             "(summed over 8 XCDs), dispatches of 200 us or more (shorter ones read above "
+             "the 2.4 GHz peak: the counter window outlasts the kernel)",
+             f"# command: {command}",
+             f"# kernel_source_hash = {kernel_source_hash()}",
+             f"{'kernel':40s} {'grid':>10s} {'n':>4s} {'med_us':>9s} {'clk_GHz':>8s} "
+             f"{'min_GHz':>8s} {'max_GHz':>8s} {'kcycles':>9s} {'corr(dur,clk)':>14s}"]
+    for name, grid, n, d, c, lo, hi, cyc, r in clock_stats(db):
+        lines.append(f"{name[:40]:40s} {grid:10d} {n:4d} {d:9.2f} {c:8.3f} {lo:8.3f} {hi:8.3f} "
+                     f"{cyc:9.1f} {r:14.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -207,9 +263,15 @@ def main():
     c.add_argument("--source", default=None,
                    help="csrc file defining the kernel; its translation unit is hashed")
     c.add_argument("--command", default="")
+    k = sub.add_parser("clock")
+    k.add_argument("db")
+    k.add_argument("out")
+    k.add_argument("--command", default="")
     a = ap.parse_args()
     if a.cmd == "trace":
         write_trace(a.db, a.out, a.command)
+    elif a.cmd == "clock":
+        write_clock(a.db, a.out, a.command)
     else:
         write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command,
                       a.grid, a.source, a.calib_default)

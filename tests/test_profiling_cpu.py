@@ -51,3 +51,29 @@ def test_unit_hash_sees_included_headers_only(csrc_copy):
     _edit(csrc_copy / "dit_rows.hpp", "namespace dit {", "namespace dit {\nconstexpr int kX = 2;")
     assert profiling.kernel_source_hash("dit_ln.hip") != h_ln      # dit_ln.hip includes it
     assert profiling.kernel_source_hash("dit_qkv.hip") == h_qkv    # dit_qkv.hip does not
+
+
+def test_clock_stats_from_a_grbm_count_table(tmp_path):
+    """Effective clock = GRBM_COUNT / 8 XCDs / duration; a kernel whose
+    dispatches all take the same core cycles shows a correlation of -1."""
+    import sqlite3
+    from modulation_bf16_row_amd import profiling
+    db = str(tmp_path / "c.db")
+    con = sqlite3.connect(db)
+    con.execute("create table counters_collection (dispatch_id int, kernel_name text, "
+                "grid_size int, counter_name text, value real, duration real)")
+    cycles = 1.0e6                                    # per XCD
+    for i, ghz in enumerate([2.0, 2.1, 2.2, 2.3, 2.4]):
+        dur_ns = cycles / ghz
+        con.execute("insert into counters_collection values (?, ?, ?, ?, ?, ?)",
+                    (i, "void dit::k_a<1>(dit::Args)", 64, "GRBM_COUNT", 8 * cycles, dur_ns))
+    con.execute("insert into counters_collection values (9, 'void k_short()', 64, 'GRBM_COUNT', "
+                "8.0, 1000.0)")                        # 1 us: below the 200 us floor
+    con.commit()
+    rows = profiling.clock_stats(db)
+    assert len(rows) == 1
+    name, grid, n, med_us, clk, lo, hi, kcyc, r = rows[0]
+    assert (name, grid, n) == ("k_a<1>", 64, 5)
+    assert abs(clk - 2.2) < 1e-9 and abs(lo - 2.0) < 1e-9 and abs(hi - 2.4) < 1e-9
+    assert abs(kcyc - 1000.0) < 1e-6
+    assert r < -0.99
