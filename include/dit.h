@@ -59,8 +59,9 @@
  *   modes.  Elsewhere the hardware rsqrt reads a subnormal argument as zero
  *   (result +inf); LayerNorm and the Q/K norm only reach that with
  *   eps < 2^-126.
- * Reduction order R(D) (D <= 8192, D % 8 == 0).  A 64-lane wave holds one
- *   row; lane l owns elements 512c + 8l + j (j = 0..7) of chunk c.  Each lane
+ * Reduction order R(D) (D <= 8192, D % 8 == 0), defined on 64 lanes (the
+ *   kernels may spread a row over several waves; the order is the same):
+ *   lane l owns elements 512c + 8l + j (j = 0..7) of chunk c.  Each lane
  *   adds its own terms to +0 in (c, j) order; then, for m = 1, 2, 4, 8, 16,
  *   32, every lane adds the partial of lane l XOR m.  Q/K head sums use the
  *   same rule with 16 lanes (8 elements each, Dh = 128) and m = 1, 2, 4, 8.
