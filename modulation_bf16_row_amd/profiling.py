@@ -20,6 +20,12 @@
       fixed number of core cycles: the dispatch is bound by the core clock,
       not by HBM)
 
+  python -m modulation_bf16_row_amd.profiling counters RESULTS.db OUT.txt --command "..."
+      per kernel, from a --pmc run of any counters: the median value of each
+      counter per dispatch, and per work-item of the dispatch (for the
+      shader instruction counters, which count wave instructions, times 64
+      gives instructions per lane)
+
 The traffic summary records a hash of the code of the kernel's translation
 unit (--source) or of all kernel sources; the benchmark only
 reports it while the sources still match.
@@ -242,6 +248,44 @@ def write_clock(db, out, command):
     print("\n".join(lines))
 
 
+def counter_table(db):
+    """{(kernel, grid): {counter: median value per dispatch}} over every
+    counter of a --pmc run."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, grid_size, counter_name, value from "
+                       "counters_collection").fetchall()
+    by = {}
+    for name, grid, cn, v in rows:
+        by.setdefault((_short(name), int(grid)), {}).setdefault(cn, []).append(float(v))
+    return {k: {cn: statistics.median(vs) for cn, vs in d.items()} for k, d in by.items()}
+
+
+def write_counters(db, out, command, min_dispatches=4):
+    table = counter_table(db)
+    names = sorted({cn for d in table.values() for cn in d})
+    lines = ["# shader counters per dispatch from rocprofv3 --pmc (median over dispatches); "
+             "'/item' divides by the dispatch's work-items (x 64 = per lane for wave counts)",
+             f"# command: {command}",
+             f"# kernel_source_hash = {kernel_source_hash()}",
+             f"{'kernel':40s} {'grid':>10s} " + " ".join(f"{n:>16s} {n[-8:] + '/item':>16s}"
+                                                         for n in names)]
+    con = sqlite3.connect(db)
+    counts = dict(((_short(n), int(g)), c) for n, g, c in con.execute(
+        "select kernel_name, grid_size, count(distinct dispatch_id) from counters_collection "
+        "group by kernel_name, grid_size").fetchall())
+    for (name, grid), d in sorted(table.items(), key=lambda kv: -kv[0][1]):
+        if not name.startswith("k_") or counts.get((name, grid), 0) < min_dispatches:
+            continue
+        cells = []
+        for n in names:
+            v = d.get(n)
+            cells.append(f"{v:16.0f} {v / grid:16.4f}" if v is not None else f"{'-':>16s} {'-':>16s}")
+        lines.append(f"{name[:40]:40s} {grid:10d} " + " ".join(cells))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -263,6 +307,10 @@ def main():
     c.add_argument("--source", default=None,
                    help="csrc file defining the kernel; its translation unit is hashed")
     c.add_argument("--command", default="")
+    q = sub.add_parser("counters")
+    q.add_argument("db")
+    q.add_argument("out")
+    q.add_argument("--command", default="")
     k = sub.add_parser("clock")
     k.add_argument("db")
     k.add_argument("out")
@@ -272,6 +320,8 @@ def main():
         write_trace(a.db, a.out, a.command)
     elif a.cmd == "clock":
         write_clock(a.db, a.out, a.command)
+    elif a.cmd == "counters":
+        write_counters(a.db, a.out, a.command)
     else:
         write_traffic(a.fetch_db, a.write_db, a.out, a.kernel, a.calib, a.calib_bytes, a.command,
                       a.grid, a.source, a.calib_default)

@@ -77,3 +77,20 @@ def test_clock_stats_from_a_grbm_count_table(tmp_path):
     assert abs(clk - 2.2) < 1e-9 and abs(lo - 2.0) < 1e-9 and abs(hi - 2.4) < 1e-9
     assert abs(kcyc - 1000.0) < 1e-6
     assert r < -0.99
+
+
+def test_counter_table_medians_per_kernel(tmp_path):
+    import sqlite3
+    from modulation_bf16_row_amd import profiling
+    db = str(tmp_path / "q.db")
+    con = sqlite3.connect(db)
+    con.execute("create table counters_collection (dispatch_id int, kernel_name text, "
+                "grid_size int, counter_name text, value real)")
+    for d, v in enumerate([100.0, 300.0, 200.0]):
+        con.execute("insert into counters_collection values (?, ?, ?, ?, ?)",
+                    (d, "void dit::k_b<2>(dit::Args)", 128, "SQ_INSTS_VALU", v))
+        con.execute("insert into counters_collection values (?, ?, ?, ?, ?)",
+                    (d, "void dit::k_b<2>(dit::Args)", 128, "SQ_WAVES", 2.0))
+    con.commit()
+    t = profiling.counter_table(db)
+    assert t == {("k_b<2>", 128): {"SQ_INSTS_VALU": 200.0, "SQ_WAVES": 2.0}}
