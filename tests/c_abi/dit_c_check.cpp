@@ -1,8 +1,9 @@
 // dit_c_check.cpp -- the epilogue library driven through its C ABI alone (no
 // Python, no torch): device buffers from hipMalloc, calls on a HIP stream,
-// results compared bit for bit with the CPU oracle (test infrastructure,
-// linked beside the library; the two share no code).  Also checks that the
-// guards' statuses reach a C caller.  Exit status 0 when every case passes.
+// every entry point of dit.h and dit_producers.h, results compared bit for
+// bit with the CPU oracle (test infrastructure, linked beside the library;
+// the two share no code).  Also checks that the guards' statuses reach a C
+// caller.  Exit status 0 when every case passes.
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -79,6 +80,20 @@ void expect_equal(const char *what, const std::vector<uint16_t> &got,
     ++g_fail;
     printf("FAIL %s: %zu of %zu differ (first at %zu: got 0x%04x, oracle 0x%04x)\n", what, bad,
            ref.size(), first, got[first], ref[first]);
+  } else {
+    printf("ok   %s (%zu elements)\n", what, ref.size());
+  }
+}
+
+template <class T>
+void expect_same_bits(const char *what, const std::vector<T> &got, const std::vector<T> &ref) {
+  ++g_cases;
+  size_t bad = 0, first = 0;
+  for (size_t i = 0; i < ref.size(); ++i)
+    if (got[i] != ref[i] && bad++ == 0) first = i;
+  if (bad) {
+    ++g_fail;
+    printf("FAIL %s: %zu of %zu differ (first at %zu)\n", what, bad, ref.size(), first);
   } else {
     printf("ok   %s (%zu elements)\n", what, ref.size());
   }
@@ -166,7 +181,81 @@ void row_ops(hipStream_t s, int64_t rows, int64_t dim, int64_t rs, bool per_toke
   compare("gate_add_ln_modulate r'", dout2, ref2);
   compare("gate_add_ln_modulate out", dout, ref);
 
+  expect_status("dit_modulate_scale_shift call",
+                dit_modulate_scale_shift(dout, rs, dx, rs, dsc, dsh, dim, mrows, rows, dim,
+                                         DIT_MODE_LOSSLESS, s), DIT_OK);
+  HIP_CHECK(hipStreamSynchronize(s));
+  orc_modulate_scale_shift(ref.data(), rs, x.data(), rs, sc.data(), sh.data(), dim, mrows, rows,
+                           dim);
+  compare("modulate_scale_shift", dout, ref);
+
+  // E4M3 copies: byte rows, row stride rounded up to a multiple of 8
+  const int64_t rs8 = (dim + 15) / 8 * 8;
+  const float fs = 0.05f;
+  float *dfs = to_dev(std::vector<float>{fs});
+  uint8_t *d8 = nullptr;
+  HIP_CHECK(hipMalloc(&d8, rows * rs8));
+  std::vector<uint8_t> ref8(rows * rs8, 0);
+  auto compare8 = [&](const char *op) {
+    auto got = to_host(d8, rows * rs8);
+    std::vector<uint8_t> gv, rv;
+    for (int64_t i = 0; i < rows; ++i)
+      for (int64_t j = 0; j < dim; ++j) {
+        gv.push_back(got[i * rs8 + j]);
+        rv.push_back(ref8[i * rs8 + j]);
+      }
+    char what[160];
+    snprintf(what, sizeof what, "%s E4M3 %s", op, tag);
+    expect_same_bits(what, gv, rv);
+  };
+  expect_status("dit_ln_modulate_fp8 call",
+                dit_ln_modulate_fp8(dout, rs, d8, rs8, dx, rs, dsc, dsh, dim, mrows, rows, dim,
+                                    eps, dfs, DIT_MODE_LOSSLESS, s), DIT_OK);
+  HIP_CHECK(hipStreamSynchronize(s));
+  orc_ln_modulate_fp8(ref.data(), rs, ref8.data(), rs8, x.data(), rs, sc.data(), sh.data(), dim,
+                      mrows, rows, dim, eps, fs);
+  compare("ln_modulate_fp8", dout, ref);
+  compare8("ln_modulate_fp8");
+  expect_status("dit_gate_add_ln_modulate_fp8 call",
+                dit_gate_add_ln_modulate_fp8(dout2, rs, dout, rs, d8, rs8, dres, rs, dx, rs, dg,
+                                             dsc, dsh, dim, mrows, rows, dim, eps, dfs,
+                                             DIT_MODE_LOSSLESS, s), DIT_OK);
+  HIP_CHECK(hipStreamSynchronize(s));
+  orc_gate_add_ln_modulate_fp8(ref2.data(), rs, ref.data(), rs, ref8.data(), rs8, res.data(), rs,
+                               x.data(), rs, g.data(), sc.data(), sh.data(), dim, mrows, rows,
+                               dim, eps, fs);
+  compare("gate_add_ln_modulate_fp8 r'", dout2, ref2);
+  compare("gate_add_ln_modulate_fp8 out", dout, ref);
+  compare8("gate_add_ln_modulate_fp8");
+  HIP_CHECK(hipFree(d8));
+  HIP_CHECK(hipFree(dfs));
+
   for (uint16_t *p : {dx, dres, dsc, dsh, dg, dw, dout, dout2}) HIP_CHECK(hipFree(p));
+}
+
+// The Wan modulation table on [1, 37 tokens, 6, 1040].
+void mod_table(hipStream_t s) {
+  const int64_t B = 1, T = 37, K = 6, D = 1040;
+  std::vector<float> table(K * D);
+  for (auto &v : table) v = (float)((int)(next_u32() % 2001) - 1000) / 4096.0f;
+  auto temb = rnd_vec(B * T * K * D, 118, 129);
+  float *dt = to_dev(table);
+  uint16_t *de = to_dev(temb);
+  float *dout = nullptr;
+  HIP_CHECK(hipMalloc(&dout, K * B * T * D * sizeof(float)));
+  expect_status("dit_wan_modulation_table call",
+                dit_wan_modulation_table(dout, dt, de, B, T, K, D, s), DIT_OK);
+  HIP_CHECK(hipStreamSynchronize(s));
+  std::vector<float> ref(K * B * T * D);
+  orc_wan_mod_table(ref.data(), table.data(), temb.data(), B, T, K, D);
+  auto got = to_host(dout, ref.size());
+  std::vector<uint32_t> gb(ref.size()), rb(ref.size());
+  memcpy(gb.data(), got.data(), gb.size() * 4);
+  memcpy(rb.data(), ref.data(), rb.size() * 4);
+  expect_same_bits("wan_modulation_table [6, 1, 37, 1040]", gb, rb);
+  HIP_CHECK(hipFree(dt));
+  HIP_CHECK(hipFree(de));
+  HIP_CHECK(hipFree(dout));
 }
 
 void qkv(hipStream_t s) {
@@ -185,10 +274,10 @@ void qkv(hipStream_t s) {
   HIP_CHECK(hipMalloc(&q, n * 2));
   HIP_CHECK(hipMalloc(&k, n * 2));
   HIP_CHECK(hipMalloc(&v, n * 2));
-  dit_qkv_stream_t ts{dt, dt + H * Dh, dt + 2 * H * Dh, W, st * W, dw, dw + Dh, st};
-  dit_qkv_stream_t is{di, di + H * Dh, di + 2 * H * Dh, W, si * W, dw + 2 * Dh, dw + 3 * Dh, si};
+  dit_qkv_stream_t ts_{dt, dt + H * Dh, dt + 2 * H * Dh, W, st * W, dw, dw + Dh, st};
+  dit_qkv_stream_t is_{di, di + H * Dh, di + 2 * H * Dh, W, si * W, dw + 2 * Dh, dw + 3 * Dh, si};
   expect_status("dit_qk_norm_rope call",
-                dit_qk_norm_rope(q, k, v, H * Dh, S * H * Dh, &ts, &is, dc, dz, B, H, Dh, 1e-6f,
+                dit_qk_norm_rope(q, k, v, H * Dh, S * H * Dh, &ts_, &is_, dc, dz, B, H, Dh, 1e-6f,
                                  DIT_MODE_LOSSLESS, s), DIT_OK);
   HIP_CHECK(hipStreamSynchronize(s));
   std::vector<uint16_t> rq(n), rk(n), rv(n);
@@ -201,6 +290,22 @@ void qkv(hipStream_t s) {
   expect_equal("qk_norm_rope q [2, 3+5, 3, 128]", to_host(q, n), rq);
   expect_equal("qk_norm_rope k [2, 3+5, 3, 128]", to_host(k, n), rk);
   expect_equal("qk_norm_rope v [2, 3+5, 3, 128]", to_host(v, n), rv);
+
+  // destination-major: P = 3 destinations of one head each, packed
+  // [P][B, S, 3, 1, 128]
+  const int64_t hpd = 1, ts = 3 * hpd * Dh, bs = S * ts, ds = B * bs, np = (H / hpd) * ds;
+  uint16_t *buf = nullptr;
+  HIP_CHECK(hipMalloc(&buf, np * 2));
+  expect_status("dit_qk_norm_rope_dest call",
+                dit_qk_norm_rope_dest(buf, buf + hpd * Dh, buf + 2 * hpd * Dh, ts, bs, hpd, ds,
+                                      &ts_, &is_, dc, dz, B, H, Dh, 1e-6f, DIT_MODE_LOSSLESS, s),
+                DIT_OK);
+  HIP_CHECK(hipStreamSynchronize(s));
+  std::vector<uint16_t> rp(np, 0);
+  orc_qk_norm_rope_dest(rp.data(), rp.data() + hpd * Dh, rp.data() + 2 * hpd * Dh, ts, bs, hpd,
+                        ds, &ot, &oi, cs.data(), sn.data(), B, H, Dh, 1e-6f);
+  expect_equal("qk_norm_rope_dest packed [3][2, 8, 3, 1, 128]", to_host(buf, np), rp);
+  HIP_CHECK(hipFree(buf));
   for (void *p : {(void *)dt, (void *)di, (void *)dw, (void *)dc, (void *)dz, (void *)q,
                   (void *)k, (void *)v})
     HIP_CHECK(hipFree(p));
@@ -239,6 +344,7 @@ int main() {
   row_ops(s, 9, 8192, 8192, true);
   row_ops(s, 64, 3072, 3072, false);
   qkv(s);
+  mod_table(s);
   statuses(s);
   HIP_CHECK(hipStreamDestroy(s));
   printf("c-abi check: %d cases, %d failed\n", g_cases, g_fail);

@@ -1,11 +1,14 @@
 """The library driven from C: tests/c_abi/dit_c_check (built by
 __graft_entry__.build()) calls the C entry points with hipMalloc'd buffers on
 a HIP stream, with no Python or torch in the process, and compares every
-output bit for bit with the CPU oracle.  Cases: LN + AdaLN modulate,
-RMSNorm-scale, RMSNorm-tanh-residual, residual gate-add and the gated
-residual + LN producer on [37 x 1032] (strided and per-token), [9 x 8192]
-and [64 x 3072]; Q/K RMSNorm + RoPE on two streams of a [2, 3+5, 3, 128]
-joint buffer; and the statuses of bad calls as a C caller sees them."""
+output bit for bit with the CPU oracle.  Every entry point of dit.h and
+dit_producers.h: LN + AdaLN modulate, RMSNorm-scale, RMSNorm-tanh-residual,
+residual gate-add, standalone modulate, the gated residual + LN producer
+and both E4M3 producers (codes byte for byte) on [37 x 1032] (strided and
+per-token), [9 x 8192] and [64 x 3072]; Q/K RMSNorm + RoPE on two streams
+of a [2, 3+5, 3, 128] joint buffer and its destination-major form (three
+destinations); the Wan modulation table on [6, 1, 37, 1040]; and the
+statuses of bad calls as a C caller sees them."""
 import os
 import re
 import subprocess
