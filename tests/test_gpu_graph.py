@@ -3,7 +3,9 @@ eager calls (and the oracle).
 
 The graph test replays a captured step -- the five epilogues, the fused
 producers (with their E4M3 copies), the standalone modulate, the
-destination-major QKV epilogue and the Wan modulation table -- several
+destination-major QKV epilogue and the Wan modulation table, and the row
+epilogues again with per-token modulation (the split-row layout, and
+tanh-residual's per-token row layout) -- several
 times, with eager work and synchronisations in between (inputs and the
 E4M3 scale are rewritten in place before each replay, so a replay must read
 the new values), and checks every replay against eager results.
@@ -77,6 +79,12 @@ class Step:
         self.temb = (torch.randn((2, 40, 6, 256), device="cuda", generator=g) * 0.3).to(
             torch.bfloat16)
         self.mt = torch.empty((6, 2, 40, 256), dtype=torch.float32, device="cuda")
+        # per-token modulation rows (the split-row layout)
+        self.sct = dev(synth.normal_bf16(tuple(self.x.shape), 0.1, seed + 21))
+        self.sht = dev(synth.normal_bf16(tuple(self.x.shape), 0.1, seed + 22))
+        self.gt = dev(synth.normal_bf16(tuple(self.x.shape), 0.1, seed + 23))
+        for k in ("lnpt", "rmspt", "tanhpt", "rppt", "glnpt"):
+            self.out[k] = torch.empty_like(self.x)
 
     def run(self, prepare=False):
         M = m()
@@ -104,6 +112,15 @@ class Step:
             M.dit_qk_norm_rope_packed(self.txt, self.img, self.cos, self.sin, 2, EPS,
                                       out=self.packed, prepare=prepare),
             M.dit_wan_modulation_table(self.table, self.temb, out=self.mt, prepare=prepare),
+            M.dit_ln_modulate(self.x, self.sct, self.sht, EPS, out=self.out["lnpt"],
+                              prepare=prepare),
+            M.dit_rmsnorm_scale(self.x, self.w, self.sct, EPS, out=self.out["rmspt"],
+                                prepare=prepare),
+            M.dit_rmsnorm_tanh_residual(self.x, self.res, self.w, self.gt, EPS,
+                                        out=self.out["tanhpt"], prepare=prepare),
+            M.dit_gate_add_ln_modulate(self.res, self.y, self.gt, self.sct, self.sht, EPS,
+                                       out_residual=self.out["rppt"], out=self.out["glnpt"],
+                                       prepare=prepare),
         ]
         return calls
 
@@ -113,7 +130,8 @@ class Step:
             [host(t) for t in self.qkv_out] + \
             [host(self.out[k]) for k in ("rp", "gln", "ln8b", "grp8", "gln8", "mod")] + \
             [self.q8[k].cpu().numpy() for k in ("ln8", "gln8")] + \
-            [host(self.packed), self.mt.cpu().numpy().view(np.uint32)]
+            [host(self.packed), self.mt.cpu().numpy().view(np.uint32)] + \
+            [host(self.out[k]) for k in ("lnpt", "rmspt", "tanhpt", "rppt", "glnpt")]
 
     def clear(self):
         for t in list(self.out.values()) + list(self.qkv_out) + list(self.q8.values()) + \
@@ -168,3 +186,5 @@ def test_graph_replays_match_eager():
                           f"replay {rep} ln vs oracle")
         ref8 = oracle.ln_modulate_fp8(xn, w["scale"], w["shift"], EPS, 0.05 * (rep + 1))
         assert np.array_equal(got[13], ref8[1]), f"replay {rep} E4M3 copy vs oracle"
+        assert_bits_equal(got[17], oracle.ln_modulate(xn, host(s.sct), host(s.sht), EPS),
+                          f"replay {rep} per-token ln vs oracle")
